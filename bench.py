@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the MegaMoE expert pipeline on one MI355X.
+
+One step = one pass of the whole hot path (route sort + quant scatter, GMM1,
+SwiGLU + re-quant, GMM2, combine + unpermute) over one batch of synthetic
+inputs already resident in HBM.  The default workload is the decode-size
+forward (M=128, K=7168, E=32, top-k 8, I=2048).  Prints ONE JSON line.
+
+Timing: W untimed warm-up steps, then K timed steps between two device
+synchronisations.  The timed steps call the per-stage entry points of the C
+ABI (the same kernels, in the same order, as megamoe_forward, which the GPU
+tests show to be bit-identical) with HIP events recorded on the launch stream
+between the stages, so per-kernel durations come from the same timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + GMM int8 TOPS (% MFMA peak), 1x MI355X"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s (no sparsity)
+STAGES = ["permute", "gmm1", "swiglu", "gmm2", "unpermute"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens of the workload the oracle runs for the CPU baseline")
+    return ap.parse_args()
+
+
+def algorithmic(w, counts: np.ndarray) -> dict:
+    """Bytes each stage must move and ops each GEMM must do (every input read
+    once, every output written once, weights of the active experts once)."""
+    R, K, I, E = w.R, w.K, w.I, w.E
+    act = int(np.count_nonzero(counts))
+    b = {}
+    # sort reads expert ids, writes 2 index arrays + counts; quant reads x once,
+    # writes topK int8 rows + scales
+    b["permute"] = R * 4 + 2 * R * 4 + 2 * E * 4 + w.M * K * 2 + R * K + R * 4
+    b["gmm1"] = act * K * 2 * I + R * K + R * 2 * I * 2 + E * 2 * I * 4
+    b["swiglu"] = R * 2 * I * 2 + R * 4 + R * I + R * 4
+    b["gmm2"] = act * I * K + R * I + R * K * 2 + E * K * 4
+    b["unpermute"] = R * K * 2 + R * 4 + R * 4 + R * 4 + w.M * K * 2
+    ops = {"gmm1": 2 * R * K * 2 * I, "gmm2": 2 * R * I * K}
+    return {"bytes": b, "ops": ops}
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str, workload: str, stage: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if the profile on
+    record was taken from the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except Exception:  # noqa: BLE001
+        return None
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, n_tokens: int | None):
+    from oracle import oracle as O
+    M = w.M if n_tokens is None else min(n_tokens, w.M)
+    sub = dict(inp)
+    for k in ("x", "expert_idx", "probs"):
+        sub[k] = np.ascontiguousarray(inp[k][:M])
+    t0 = time.perf_counter()
+    O.forward(sub, E=w.E)
+    dt = time.perf_counter() - t0
+    return {"value": M / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{M} of {w.M} tokens of the {w.name} workload (all their routes, "
+                      f"all stages), single-threaded C oracle, {dt:.1f} s",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {a.gpus} requested); the "
+              "expert-parallel split across GPUs is not implemented here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from moe_expert_ffn_amd import inputs as W
+    from moe_expert_ffn_amd import megamoe as MM
+
+    w = W.WORKLOADS[a.workload]
+    inp = W.generate(w, a.seed)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda") for k, v in inp.items()}
+    d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
+    n1, n2 = MM.megamoe_packed_weight_bytes(d)
+    w1p = torch.empty(n1, dtype=torch.int8, device="cuda")
+    w2p = torch.empty(n2, dtype=torch.int8, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    MM.megamoe_prepack_w1(d, dev["w1"], w1p)
+    MM.megamoe_prepack_w2(d, dev["w2"], w2p)
+    torch.cuda.synchronize()
+    prepack_ms = (time.perf_counter() - t0) * 1e3
+    del dev["w1"], dev["w2"]
+
+    R = w.R
+    f = dict(device="cuda")
+    gmA = torch.empty((R, w.K), dtype=torch.int8, **f)
+    pts1 = torch.empty(R, dtype=torch.float32, **f)
+    eri = torch.empty(R, dtype=torch.int32, **f)
+    srt = torch.empty(R, dtype=torch.int32, **f)
+    cnt = torch.empty(w.E, dtype=torch.int32, **f)
+    cum = torch.empty(w.E, dtype=torch.int32, **f)
+    gmC = torch.empty((R, w.N1), dtype=torch.float16, **f)
+    q2 = torch.empty((R, w.I), dtype=torch.int8, **f)
+    pts2 = torch.empty(R, dtype=torch.float32, **f)
+    g2 = torch.empty((R, w.K), dtype=torch.float16, **f)
+    out = torch.empty((w.M, w.K), dtype=torch.bfloat16, **f)
+    pws = torch.empty(MM.megamoe_permute_workspace_bytes(d), dtype=torch.uint8, **f)
+    fws = torch.empty(MM.megamoe_workspace_bytes(d), dtype=torch.uint8, **f)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        MM.megamoe_permute(d, dev["x"], dev["expert_idx"], gmA, pts1, eri, srt, cnt, cum, pws)
+        if ev is not None:
+            ev[1].record(stream)
+        MM.megamoe_gmm1(d, gmA, cum, w1p, dev["scale1"], gmC)
+        if ev is not None:
+            ev[2].record(stream)
+        MM.megamoe_swiglu_quant(d, gmC, pts1, cum, q2, pts2)
+        if ev is not None:
+            ev[3].record(stream)
+        MM.megamoe_gmm2(d, q2, cum, w2p, dev["scale2"], g2)
+        if ev is not None:
+            ev[4].record(stream)
+        MM.megamoe_unpermute(d, g2, pts2, eri, dev["probs"], out)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / a.steps
+    stage_ms = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
+                                  for i in range(a.steps)])) for j, s in enumerate(STAGES)}
+    stage_min = {s: float(np.min([events[i][j].elapsed_time(events[i][j + 1])
+                                  for i in range(a.steps)])) for j, s in enumerate(STAGES)}
+
+    # the single-call forward, for reference (same kernels)
+    for _ in range(2):
+        MM.megamoe_forward(d, dev["x"], dev["expert_idx"], dev["probs"], w1p, dev["scale1"], w2p,
+                           dev["scale2"], out, fws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.steps):
+        MM.megamoe_forward(d, dev["x"], dev["expert_idx"], dev["probs"], w1p, dev["scale1"], w2p,
+                           dev["scale2"], out, fws)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t1) * 1e3 / a.steps
+
+    counts = cnt.cpu().numpy()
+    alg = algorithmic(w, counts)
+    stages = {}
+    for s in STAGES:
+        ms = stage_ms[s]
+        e = {"ms": round(ms, 4), "ms_min": round(stage_min[s], 4),
+             "alg_bytes": alg["bytes"][s],
+             "GBps": round(alg["bytes"][s] / (ms * 1e-3) / 1e9, 1),
+             "hbm_frac": round(alg["bytes"][s] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if s in alg["ops"]:
+            tops = alg["ops"][s] / (ms * 1e-3) / 1e12
+            e.update({"ops": alg["ops"][s], "TOPS": round(tops, 1),
+                      "mfma_frac": round(tops / PEAK_INT8_TOPS, 4)})
+        stages[s] = e
+
+    # dominant kernel: the stage with the largest share of the step
+    dom = max(STAGES, key=lambda s: stage_ms[s])
+    gemm_src = os.path.join(ROOT, "moe_expert_ffn_amd", "csrc", "gmm.hip")
+    dom_src = {"permute": "permute.hip", "gmm1": "gmm.hip", "gmm2": "gmm.hip",
+               "swiglu": "swiglu.hip", "unpermute": "unpermute.hip"}[dom]
+    dom_src = os.path.join(ROOT, "moe_expert_ffn_amd", "csrc", dom_src)
+    ms = stage_ms[dom]
+    ai = alg["ops"].get(dom, 0) / alg["bytes"][dom]
+    if dom in alg["ops"] and ai > PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(alg["ops"][dom] / (ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_INT8_TOPS, "unit": "TOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(alg["bytes"][dom] / (ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic_from_profile(dom_src, w.name, dom)
+    roof["kernel"] = dom
+    del gemm_src
+
+    gmm_ops = alg["ops"]["gmm1"] + alg["ops"]["gmm2"]
+    gmm_ms = stage_ms["gmm1"] + stage_ms["gmm2"]
+    gmm_tops = gmm_ops / (gmm_ms * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": round(w.M / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "K": w.K, "E": w.E, "top_k": w.top_k,
+                   "I": w.I, "routing": w.routing, "seed": a.seed},
+        "roofline": roof,
+        "gmm_int8_tops": round(gmm_tops, 1),
+        "gmm_mfma_frac": round(gmm_tops / PEAK_INT8_TOPS, 4),
+        "forward_call_ms_per_step": round(fwd_ms, 4),
+        "prepack_ms": round(prepack_ms, 2),
+        "stages": stages,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

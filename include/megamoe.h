@@ -1,0 +1,149 @@
+/*
+ * megamoe.h -- C ABI of the MI355X (gfx950) MegaMoE expert pipeline, one rank.
+ *
+ * The pipeline is the one described on the "pto-isa MegaMoE operator" overview
+ * page (pto-isa, kernels/manual/a2a3/dispatch_mega_combine), stage overview
+ * and sections 1-7: FrontReorder -> (Dispatch) -> GMM1 -> SwiGLU -> GMM2 ->
+ * (Combine) -> Unpermute.  With a single rank, Dispatch is the identity (the
+ * quantised rows are written straight into the expert-major A matrix) and
+ * Combine's remote store becomes the dequant-and-cast that Unpermute applies
+ * in registers.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or synchronises on the forward path; all work is
+ *    enqueued in order on `stream` (a hipStream_t; NULL = default stream).
+ *  - Tensors are dense, row-major, and 16-byte aligned.
+ *  - fp16 and bf16 tensors are passed as uint16_t bit patterns.
+ *  - Routes are numbered r = t * top_k + s (token t, slot s).  R = M * top_k.
+ *  - Argument errors are reported synchronously by the return code and leave
+ *    nothing enqueued.  A kernel launch failure returns MEGAMOE_EHIP.
+ *  - Expert ids outside [0, E) cannot be checked without a device sync: such
+ *    a route is dropped (expanded_row_idx = -1, not counted, skipped by the
+ *    combine) and counted in a device error word kept in the workspace, which
+ *    megamoe_last_error() reads.
+ *  - The library is reentrant: calls with distinct buffers may run on
+ *    distinct streams concurrently.
+ *
+ * Shape limits (checked): 1 <= M; 1 <= top_k <= E <= 256; K % 128 == 0,
+ * 128 <= K <= 32768; I % 128 == 0, 128 <= I <= 16384; R * max(K, 2I) < 2^31.
+ */
+#ifndef MEGAMOE_H_
+#define MEGAMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MEGAMOE_OK = 0,
+    MEGAMOE_EINVAL = 1,        /* bad pointer, bad dims, misaligned tensor   */
+    MEGAMOE_EUNSUPPORTED = 2,  /* dims outside the supported limits          */
+    MEGAMOE_EWORKSPACE = 3,    /* workspace smaller than required            */
+    MEGAMOE_EHIP = 4           /* a HIP runtime call or launch failed        */
+} megamoe_status;
+
+/* M tokens, hidden size K, E local experts, top_k routes per token, and the
+ * SwiGLU output width I (GMM1 produces N = 2I columns: [0, I) go through
+ * silu and [I, 2I) are the gate; GMM2 reduces over I back to K). */
+typedef struct {
+    int32_t M, K, E, top_k, I;
+} megamoe_dims;
+
+/* Human-readable text of a status code (static storage). */
+const char *megamoe_strerror(int status);
+
+/* Validates dims against the shape limits.  Returns MEGAMOE_OK or an error. */
+int megamoe_check_dims(const megamoe_dims *d);
+
+/* Bytes of workspace megamoe_forward needs (intermediates + error word).
+ * megamoe_permute needs only megamoe_permute_workspace_bytes. */
+int megamoe_workspace_bytes(const megamoe_dims *d, size_t *bytes);
+int megamoe_permute_workspace_bytes(const megamoe_dims *d, size_t *bytes);
+
+/* Bytes of the packed weights.  The packed layout is private to the library;
+ * callers only allocate it and pass it back. */
+int megamoe_packed_weight_bytes(const megamoe_dims *d, size_t *w1p_bytes, size_t *w2p_bytes);
+
+/* One-time weight layout transform (the pages feed GMM1/GMM2 from pre-packed
+ * weights; see sections 3 and 5).
+ *   w1  int8 [E, K, 2I]  logical GMM1 weight (column n of expert e = w1[e, :, n])
+ *   w2  int8 [E, I, K]   logical GMM2 weight
+ * Output buffers must be megamoe_packed_weight_bytes() long. */
+int megamoe_prepack_w1(const megamoe_dims *d, const int8_t *w1, int8_t *w1p, void *stream);
+int megamoe_prepack_w2(const megamoe_dims *d, const int8_t *w2, int8_t *w2p, void *stream);
+
+/* The whole forward (stage overview of the page):
+ *   x          fp16  [M, K]
+ *   expert_idx int32 [M, top_k]
+ *   probs      fp32  [M, top_k]   combine weights, used as given
+ *   w1p/w2p    packed weights from megamoe_prepack_w1/_w2
+ *   scale1     fp32  [E, 2I]      GMM1 per-output-channel dequant scale
+ *   scale2     fp32  [E, K]       GMM2 per-output-channel dequant scale
+ *   out        bf16  [M, K]
+ *   workspace  >= megamoe_workspace_bytes(); the caller may not touch it while
+ *              the forward runs.  Intermediates live there. */
+int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                    const float *probs, const int8_t *w1p, const float *scale1,
+                    const int8_t *w2p, const float *scale2, uint16_t *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage 1 FrontReorder (+ identity Dispatch), section 1 of the page:
+ * stable expert-major sort of the routes (ties keep ascending route order),
+ * per-expert counts, inclusive prefix over experts, inverse map, and the
+ * per-token dynamic int8 quantisation scattered to every route's row.
+ *   gmA               int8  [R, K]  expert-major rows; rows >= valid count unused
+ *   pts1              fp32  [R]     perTokenScale1 of each row
+ *   expanded_row_idx  int32 [R]     route -> row, -1 for a dropped route
+ *   sorted_route      int32 [R]     row -> route, -1 past the valid rows
+ *   tokens_per_expert int32 [E]
+ *   expert_cumsum     int32 [E]     inclusive prefix of tokens_per_expert
+ *   workspace         >= megamoe_permute_workspace_bytes() (error word) */
+int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                    int8_t *gmA, float *pts1, int32_t *expanded_row_idx, int32_t *sorted_route,
+                    int32_t *tokens_per_expert, int32_t *expert_cumsum, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Stage 3 GMM1, section 3: for every row of expert e's group,
+ *   acc[row, n] = sum_k gmA[row, k] * w1[e, k, n]   (int32, exact)
+ *   gmC[row, n] = fp16(fp32(acc) * scale1[e, n])
+ * Groups are taken from expert_cumsum (device).  gmC fp16 [R, 2I].
+ * acc_dbg (nullable) receives the int32 accumulators [R, 2I]. */
+int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert_cumsum,
+                 const int8_t *w1p, const float *scale1, uint16_t *gmC, int32_t *acc_dbg,
+                 void *stream);
+
+/* Stage 4 SwiGLU, section 4: per valid row,
+ *   c = fp32(gmC) * pts1;  y = silu(c[0:I]) * c[I:2I];  pts2 = max|y| / 127;
+ *   q2 = rint(y * (127 / max|y|))  (int8)
+ * Valid rows are [0, expert_cumsum[E-1]).  q2 int8 [R, I], pts2 fp32 [R]. */
+int megamoe_swiglu_quant(const megamoe_dims *d, const uint16_t *gmC, const float *pts1,
+                         const int32_t *expert_cumsum, int8_t *q2, float *pts2, void *stream);
+
+/* Stage 5 GMM2, section 5:
+ *   acc[row, k] = sum_i q2[row, i] * w2[e, i, k];  gmm2_out = fp16(fp32(acc) * scale2[e, k])
+ * gmm2_out fp16 [R, K]; acc_dbg (nullable) int32 [R, K]. */
+int megamoe_gmm2(const megamoe_dims *d, const int8_t *q2, const int32_t *expert_cumsum,
+                 const int8_t *w2p, const float *scale2, uint16_t *gmm2_out, int32_t *acc_dbg,
+                 void *stream);
+
+/* Stages 6-7 Combine (one rank) + Unpermute, sections 6 and 7: for token t,
+ *   out[t, k] = bf16( sum_s bf16(fp32(gmm2_out[row_s, k]) * pts2[row_s]) * probs[t, s] )
+ * with row_s = expanded_row_idx[t * top_k + s], slots in order, fp32
+ * accumulation, rows < 0 skipped.  out bf16 [M, K]. */
+int megamoe_unpermute(const megamoe_dims *d, const uint16_t *gmm2_out, const float *pts2,
+                      const int32_t *expanded_row_idx, const float *probs, uint16_t *out,
+                      void *stream);
+
+/* Synchronises `stream` and reads the number of routes dropped by the last
+ * megamoe_permute / megamoe_forward that used this workspace. */
+int megamoe_last_error(const void *workspace, void *stream, int32_t *bad_route_count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEGAMOE_H_ */

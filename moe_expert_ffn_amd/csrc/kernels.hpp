@@ -1,0 +1,34 @@
+// Internal launch interface between the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace megamoe {
+
+struct GmmParams {
+    const int8_t *A;          // [rows, Kred] expert-major activations
+    const int8_t *B;          // packed weights [E][N][Kred]
+    const float *scale;       // [E][N] per-output-channel dequant scale
+    const int32_t *cumsum;    // [E] inclusive row prefix over experts
+    uint16_t *C;              // [rows, N] fp16
+    int32_t *acc_dbg;         // nullable [rows, N] int32 accumulators
+    int E, N, Kred;
+};
+
+hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *sorted_route,
+                             int32_t *expanded_row_idx, int32_t *tokens_per_expert,
+                             int32_t *expert_cumsum, int32_t *err_word, hipStream_t stream);
+hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
+                                int top_k, int8_t *gmA, float *pts1, hipStream_t stream);
+hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,
+                               const int32_t *expert_cumsum, int R, int E, int I, int8_t *q2,
+                               float *pts2, hipStream_t stream);
+hipError_t launch_unpermute(const uint16_t *gmm2_out, const float *pts2,
+                            const int32_t *expanded_row_idx, const float *probs, int M, int K,
+                            int top_k, uint16_t *out, hipStream_t stream);
+hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipStream_t stream);
+int gmm_pick_variant(int R, int E);
+hipError_t launch_gmm(int variant, const GmmParams &prm, int R, int cu_count, hipStream_t stream);
+
+}  // namespace megamoe

@@ -1,0 +1,246 @@
+// Host side of the MegaMoE C ABI: argument checks, workspace carving and the
+// launch order of the stages on one stream.  The order is the stage overview
+// of the pto-isa MegaMoE overview page: FrontReorder, (Dispatch), GMM1,
+// SwiGLU, GMM2, (Combine), Unpermute.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/megamoe.h"
+#include "kernels.hpp"
+
+
+using namespace megamoe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kErrBytes = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+int cu_count_current() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+struct Layout {
+    size_t err, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2, g2, total;
+};
+
+Layout forward_layout(const megamoe_dims &d) {
+    const size_t R = (size_t)d.M * d.top_k;
+    Layout L;
+    size_t o = 0;
+    L.err = o;    o += align_up(kErrBytes);
+    L.eri = o;    o += align_up(R * 4);
+    L.sorted = o; o += align_up(R * 4);
+    L.counts = o; o += align_up((size_t)d.E * 4);
+    L.cumsum = o; o += align_up((size_t)d.E * 4);
+    L.pts1 = o;   o += align_up(R * 4);
+    L.pts2 = o;   o += align_up(R * 4);
+    L.gmA = o;    o += align_up(R * d.K);
+    L.gmC = o;    o += align_up(R * 2 * d.I * 2);
+    L.q2 = o;     o += align_up(R * d.I);
+    L.g2 = o;     o += align_up(R * d.K * 2);
+    L.total = o;
+    return L;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_EHIP; }
+
+#define MEGAMOE_TRY(expr)                         \
+    do {                                          \
+        const int _rc = (expr);                   \
+        if (_rc != MEGAMOE_OK) return _rc;        \
+    } while (0)
+
+int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_idx, int8_t *gmA,
+                float *pts1, int32_t *eri, int32_t *sorted, int32_t *counts, int32_t *cumsum,
+                int32_t *err_word, hipStream_t s) {
+    const int R = d.M * d.top_k;
+    MEGAMOE_TRY(hip_status(launch_route_sort(expert_idx, R, d.E, sorted, eri, counts, cumsum,
+                                             err_word, s)));
+    return hip_status(launch_quant_scatter(x, eri, d.M, d.K, d.top_k, gmA, pts1, s));
+}
+
+int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const int8_t *Bp,
+            const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s) {
+    const int R = d.M * d.top_k;
+    GmmParams prm{A, Bp, scale, cumsum, C, dbg, d.E, N, Kred};
+    return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *megamoe_strerror(int status) {
+    switch (status) {
+        case MEGAMOE_OK: return "ok";
+        case MEGAMOE_EINVAL: return "invalid argument (null or misaligned pointer, bad dims)";
+        case MEGAMOE_EUNSUPPORTED: return "dims outside the supported limits";
+        case MEGAMOE_EWORKSPACE: return "workspace too small";
+        case MEGAMOE_EHIP: return "HIP runtime or launch failure";
+        default: return "unknown status";
+    }
+}
+
+int megamoe_check_dims(const megamoe_dims *d) {
+    if (!d) return MEGAMOE_EINVAL;
+    if (d->M < 1 || d->K < 1 || d->E < 1 || d->top_k < 1 || d->I < 1) return MEGAMOE_EINVAL;
+    if (d->top_k > d->E || d->E > 256) return MEGAMOE_EUNSUPPORTED;
+    if (d->K % 128 != 0 || d->K > 32768) return MEGAMOE_EUNSUPPORTED;
+    if (d->I % 128 != 0 || d->I > 16384) return MEGAMOE_EUNSUPPORTED;
+    const long long R = (long long)d->M * d->top_k;
+    const long long wide = d->K > 2 * d->I ? d->K : 2 * d->I;
+    if (R * wide >= (1ll << 31)) return MEGAMOE_EUNSUPPORTED;
+    return MEGAMOE_OK;
+}
+
+int megamoe_workspace_bytes(const megamoe_dims *d, size_t *bytes) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    if (!bytes) return MEGAMOE_EINVAL;
+    *bytes = forward_layout(*d).total;
+    return MEGAMOE_OK;
+}
+
+int megamoe_permute_workspace_bytes(const megamoe_dims *d, size_t *bytes) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    if (!bytes) return MEGAMOE_EINVAL;
+    *bytes = kErrBytes;
+    return MEGAMOE_OK;
+}
+
+int megamoe_packed_weight_bytes(const megamoe_dims *d, size_t *w1p, size_t *w2p) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    if (!w1p || !w2p) return MEGAMOE_EINVAL;
+    *w1p = (size_t)d->E * d->K * 2 * d->I;
+    *w2p = (size_t)d->E * d->I * d->K;
+    return MEGAMOE_OK;
+}
+
+int megamoe_prepack_w1(const megamoe_dims *d, const int8_t *w1, int8_t *w1p, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    if (!aligned16(w1) || !aligned16(w1p)) return MEGAMOE_EINVAL;
+    return hip_status(launch_pack(w1, w1p, d->E, d->K, 2 * d->I, (hipStream_t)stream));
+}
+
+int megamoe_prepack_w2(const megamoe_dims *d, const int8_t *w2, int8_t *w2p, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    if (!aligned16(w2) || !aligned16(w2p)) return MEGAMOE_EINVAL;
+    return hip_status(launch_pack(w2, w2p, d->E, d->I, d->K, (hipStream_t)stream));
+}
+
+int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                    int8_t *gmA, float *pts1, int32_t *eri, int32_t *sorted_route,
+                    int32_t *tokens_per_expert, int32_t *expert_cumsum, void *ws,
+                    size_t ws_bytes, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
+                          expert_cumsum, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (ws_bytes < kErrBytes) return MEGAMOE_EWORKSPACE;
+    return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
+                       expert_cumsum, (int32_t *)ws, (hipStream_t)stream);
+}
+
+int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert_cumsum,
+                 const int8_t *w1p, const float *scale1, uint16_t *gmC, int32_t *acc_dbg,
+                 void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {gmA, expert_cumsum, w1p, scale1, gmC};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (acc_dbg && !aligned16(acc_dbg)) return MEGAMOE_EINVAL;
+    return run_gmm(*d, gmA, expert_cumsum, w1p, scale1, gmC, acc_dbg, 2 * d->I, d->K,
+                   (hipStream_t)stream);
+}
+
+int megamoe_swiglu_quant(const megamoe_dims *d, const uint16_t *gmC, const float *pts1,
+                         const int32_t *expert_cumsum, int8_t *q2, float *pts2, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {gmC, pts1, expert_cumsum, q2, pts2};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    return hip_status(launch_swiglu_quant(gmC, pts1, expert_cumsum, d->M * d->top_k, d->E, d->I,
+                                          q2, pts2, (hipStream_t)stream));
+}
+
+int megamoe_gmm2(const megamoe_dims *d, const int8_t *q2, const int32_t *expert_cumsum,
+                 const int8_t *w2p, const float *scale2, uint16_t *gmm2_out, int32_t *acc_dbg,
+                 void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {q2, expert_cumsum, w2p, scale2, gmm2_out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (acc_dbg && !aligned16(acc_dbg)) return MEGAMOE_EINVAL;
+    return run_gmm(*d, q2, expert_cumsum, w2p, scale2, gmm2_out, acc_dbg, d->K, d->I,
+                   (hipStream_t)stream);
+}
+
+int megamoe_unpermute(const megamoe_dims *d, const uint16_t *gmm2_out, const float *pts2,
+                      const int32_t *eri, const float *probs, uint16_t *out, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {gmm2_out, pts2, eri, probs, out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    return hip_status(launch_unpermute(gmm2_out, pts2, eri, probs, d->M, d->K, d->top_k, out,
+                                       (hipStream_t)stream));
+}
+
+int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                    const float *probs, const int8_t *w1p, const float *scale1,
+                    const int8_t *w2p, const float *scale2, uint16_t *out, void *ws,
+                    size_t ws_bytes, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {x, expert_idx, probs, w1p, scale1, w2p, scale2, out, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    const Layout L = forward_layout(*d);
+    if (ws_bytes < L.total) return MEGAMOE_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = (char *)ws;
+    int32_t *err = (int32_t *)(base + L.err);
+    int32_t *eri = (int32_t *)(base + L.eri);
+    int32_t *sorted = (int32_t *)(base + L.sorted);
+    int32_t *counts = (int32_t *)(base + L.counts);
+    int32_t *cumsum = (int32_t *)(base + L.cumsum);
+    float *pts1 = (float *)(base + L.pts1);
+    float *pts2 = (float *)(base + L.pts2);
+    int8_t *gmA = (int8_t *)(base + L.gmA);
+    uint16_t *gmC = (uint16_t *)(base + L.gmC);
+    int8_t *q2 = (int8_t *)(base + L.q2);
+    uint16_t *g2 = (uint16_t *)(base + L.g2);
+
+    MEGAMOE_TRY(run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, s));
+    MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s));
+    MEGAMOE_TRY(hip_status(
+        launch_swiglu_quant(gmC, pts1, cumsum, d->M * d->top_k, d->E, d->I, q2, pts2, s)));
+    MEGAMOE_TRY(run_gmm(*d, q2, cumsum, w2p, scale2, g2, nullptr, d->K, d->I, s));
+    return hip_status(launch_unpermute(g2, pts2, eri, probs, d->M, d->K, d->top_k, out, s));
+}
+
+int megamoe_last_error(const void *ws, void *stream, int32_t *bad_route_count) {
+    if (!aligned16(ws) || !bad_route_count) return MEGAMOE_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MEGAMOE_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MEGAMOE_EHIP;
+    *bad_route_count = v;
+    return MEGAMOE_OK;
+}
+
+}  // extern "C"

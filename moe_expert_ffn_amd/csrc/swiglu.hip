@@ -1,0 +1,101 @@
+// SwiGLU with dynamic per-row int8 re-quantisation.
+//
+// Section 4 ("SwiGLU") of the pto-isa MegaMoE overview page: dequantise the
+// GMM1 output row with the row's perTokenScale1 (fp32), apply
+// silu(u) = u / (1 + exp(-u)) to the first half and multiply by the second
+// half, then quantise the row again: scale2 = max|y| / 127 and
+// q = CAST_RINT(y * (127 / max|y|)).
+//
+// One workgroup per row; each thread keeps its 8-column chunks of y in
+// registers so the row maximum needs a single pass over HBM.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace megamoe {
+
+template <int MAXC>
+__global__ __launch_bounds__(256) void swiglu_quant_kernel(
+    const uint16_t *__restrict__ gmC, const float *__restrict__ pts1,
+    const int32_t *__restrict__ expert_cumsum, int E, int I, int8_t *__restrict__ q2,
+    float *__restrict__ pts2) {
+    __shared__ float s_red[4];
+    const int row = blockIdx.x;
+    if (row >= expert_cumsum[E - 1]) return;  // only valid rows carry data
+    const int tid = threadIdx.x;
+    const int nchunk = I >> 3;
+    const float p1 = pts1[row];
+    const uint16_t *crow = gmC + (size_t)row * (2 * I);
+
+    float y[MAXC][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c < nchunk) {
+            const uint4 uraw = *reinterpret_cast<const uint4 *>(crow + c * 8);
+            const uint4 graw = *reinterpret_cast<const uint4 *>(crow + I + c * 8);
+            const uint32_t *uw = reinterpret_cast<const uint32_t *>(&uraw);
+            const uint32_t *gw = reinterpret_cast<const uint32_t *>(&graw);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float u = h2f((uint16_t)((uw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;
+                const float g = h2f((uint16_t)((gw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;
+                const float ex = expf(u * -1.0f);
+                const float den = ex + 1.0f;
+                const float s = u / den;
+                const float v = s * g;
+                y[i][j] = v;
+                amax = fmaxf(amax, fabsf(v));
+            }
+        }
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) s_red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float scale2 = amax / 127.0f;
+    const float mul = 127.0f / amax;
+
+    int8_t *qrow = q2 + (size_t)row * I;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c >= nchunk) continue;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int q = 0;
+            if (amax != 0.0f) {
+                float r = rintf(y[i][j] * mul);  // CAST_RINT: ties to even
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                q = (int)r;
+            }
+            if (j < 4) lo |= ((uint32_t)q & 0xffu) << (8 * j);
+            else hi |= ((uint32_t)q & 0xffu) << (8 * (j - 4));
+        }
+        *reinterpret_cast<uint2 *>(qrow + c * 8) = make_uint2(lo, hi);
+    }
+    if (tid == 0) pts2[row] = scale2;
+}
+
+hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,
+                               const int32_t *expert_cumsum, int R, int E, int I, int8_t *q2,
+                               float *pts2, hipStream_t stream) {
+    const int per_thread = (I / 8 + 255) / 256;
+    dim3 grid(R), block(256);
+    if (per_thread <= 1)
+        hipLaunchKernelGGL(swiglu_quant_kernel<1>, grid, block, 0, stream, gmC, pts1,
+                           expert_cumsum, E, I, q2, pts2);
+    else if (per_thread <= 2)
+        hipLaunchKernelGGL(swiglu_quant_kernel<2>, grid, block, 0, stream, gmC, pts1,
+                           expert_cumsum, E, I, q2, pts2);
+    else if (per_thread <= 4)
+        hipLaunchKernelGGL(swiglu_quant_kernel<4>, grid, block, 0, stream, gmC, pts1,
+                           expert_cumsum, E, I, q2, pts2);
+    else
+        hipLaunchKernelGGL(swiglu_quant_kernel<8>, grid, block, 0, stream, gmC, pts1,
+                           expert_cumsum, E, I, q2, pts2);
+    return hipGetLastError();
+}
+
+}  // namespace megamoe

@@ -1,0 +1,62 @@
+// Combine (one rank) + Unpermute.
+//
+// Sections 6 and 7 of the pto-isa MegaMoE overview page.  Combine dequantises
+// a GMM2 output row with its perTokenScale2 and casts it to the output element
+// type (bfloat16 here); Unpermute gathers, for each token, the rows of its
+// top-k routes through expandedRowIdx, weights them by probs and accumulates
+// in fp32 (slots in order, multiply then add), then rounds to the output type.
+// With one rank the combine's store-and-reload collapses into registers.
+//
+// The page found fp32 atomics slower than a gather for this step; this kernel
+// is a pure gather: each thread owns 8 output columns of one token and reads
+// the matching 16 bytes of every slot's row.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace megamoe {
+
+__global__ __launch_bounds__(256) void unpermute_kernel(
+    const uint16_t *__restrict__ gmm2_out, const float *__restrict__ pts2,
+    const int32_t *__restrict__ expanded_row_idx, const float *__restrict__ probs, int K,
+    int top_k, uint16_t *__restrict__ out) {
+    const int t = blockIdx.x;
+    const int c = blockIdx.y * 256 + threadIdx.x;  // 8-column chunk
+    if (c * 8 >= K) return;
+    const int32_t *rows = expanded_row_idx + (size_t)t * top_k;
+    const float *pr = probs + (size_t)t * top_k;
+
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+
+    for (int s = 0; s < top_k; ++s) {
+        const int d = rows[s];
+        if (d < 0) continue;  // dropped route
+        const float sc = pts2[d];
+        const float p = pr[s];
+        const uint4 raw = *reinterpret_cast<const uint4 *>(gmm2_out + (size_t)d * K + c * 8);
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float g = h2f((uint16_t)((w[j >> 1] >> ((j & 1) * 16)) & 0xffffu));
+            const float deq = bf2f(f2bf(g * sc));  // combine: cast to the output type
+            const float weighted = deq * p;
+            acc[j] = acc[j] + weighted;
+        }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = f2bf(acc[2 * j]) | (f2bf(acc[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4 *>(out + (size_t)t * K + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_unpermute(const uint16_t *gmm2_out, const float *pts2,
+                            const int32_t *expanded_row_idx, const float *probs, int M, int K,
+                            int top_k, uint16_t *out, hipStream_t stream) {
+    dim3 grid(M, (K / 8 + 255) / 256), block(256);
+    hipLaunchKernelGGL(unpermute_kernel, grid, block, 0, stream, gmm2_out, pts2, expanded_row_idx,
+                       probs, K, top_k, out);
+    return hipGetLastError();
+}
+
+}  // namespace megamoe

@@ -1,0 +1,231 @@
+"""Thin ctypes binding of the MegaMoE C ABI (include/megamoe.h).
+
+Argument marshalling only: every step of the pipeline runs in the HIP kernels
+of libmegamoe.so.  PyTorch provides device memory and the current stream.
+The functions keep the C names; tensors must be contiguous CUDA (HIP) tensors
+of the dtypes the header states.  fp16 tensors are torch.float16, bf16 tensors
+torch.bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmegamoe.so")
+
+MEGAMOE_OK = 0
+
+
+class MegaMoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({strerror(status)})")
+        self.status = status
+
+
+class megamoe_dims(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("I", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"megamoe_dims(M={self.M}, K={self.K}, E={self.E}, top_k={self.top_k}, I={self.I})"
+
+
+EXPORTED = [
+    "megamoe_strerror", "megamoe_check_dims", "megamoe_workspace_bytes",
+    "megamoe_permute_workspace_bytes", "megamoe_packed_weight_bytes", "megamoe_prepack_w1",
+    "megamoe_prepack_w2", "megamoe_forward", "megamoe_permute", "megamoe_gmm1",
+    "megamoe_swiglu_quant", "megamoe_gmm2", "megamoe_unpermute", "megamoe_last_error",
+]
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmegamoe.so.  There is no fallback: a missing library is an error."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                           "`python -m moe_expert_ffn_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, D, i32, sz = ctypes.c_void_p, ctypes.POINTER(megamoe_dims), ctypes.c_int, ctypes.c_size_t
+    psz = ctypes.POINTER(ctypes.c_size_t)
+    L.megamoe_strerror.argtypes, L.megamoe_strerror.restype = [i32], ctypes.c_char_p
+    L.megamoe_check_dims.argtypes, L.megamoe_check_dims.restype = [D], i32
+    L.megamoe_workspace_bytes.argtypes, L.megamoe_workspace_bytes.restype = [D, psz], i32
+    L.megamoe_permute_workspace_bytes.argtypes = [D, psz]
+    L.megamoe_permute_workspace_bytes.restype = i32
+    L.megamoe_packed_weight_bytes.argtypes = [D, psz, psz]
+    L.megamoe_packed_weight_bytes.restype = i32
+    L.megamoe_prepack_w1.argtypes, L.megamoe_prepack_w1.restype = [D, P, P, P], i32
+    L.megamoe_prepack_w2.argtypes, L.megamoe_prepack_w2.restype = [D, P, P, P], i32
+    L.megamoe_forward.argtypes = [D, P, P, P, P, P, P, P, P, P, sz, P]
+    L.megamoe_forward.restype = i32
+    L.megamoe_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, sz, P]
+    L.megamoe_permute.restype = i32
+    L.megamoe_gmm1.argtypes, L.megamoe_gmm1.restype = [D, P, P, P, P, P, P, P], i32
+    L.megamoe_swiglu_quant.argtypes = [D, P, P, P, P, P, P]
+    L.megamoe_swiglu_quant.restype = i32
+    L.megamoe_gmm2.argtypes, L.megamoe_gmm2.restype = [D, P, P, P, P, P, P, P], i32
+    L.megamoe_unpermute.argtypes, L.megamoe_unpermute.restype = [D, P, P, P, P, P, P], i32
+    L.megamoe_last_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
+    L.megamoe_last_error.restype = i32
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    try:
+        return load().megamoe_strerror(status).decode()
+    except Exception:  # noqa: BLE001 - message only
+        return "unknown"
+
+
+def dims(M: int, K: int, E: int, top_k: int, I: int) -> megamoe_dims:
+    return megamoe_dims(M, K, E, top_k, I)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != MEGAMOE_OK:
+        raise MegaMoEError(fn, rc)
+
+
+def _ptr(t: torch.Tensor | None, dtype: torch.dtype | None = None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def megamoe_check_dims(d: megamoe_dims) -> int:
+    return load().megamoe_check_dims(ctypes.byref(d))
+
+
+def megamoe_workspace_bytes(d: megamoe_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("megamoe_workspace_bytes", load().megamoe_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def megamoe_permute_workspace_bytes(d: megamoe_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("megamoe_permute_workspace_bytes",
+           load().megamoe_permute_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def megamoe_packed_weight_bytes(d: megamoe_dims) -> tuple[int, int]:
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("megamoe_packed_weight_bytes",
+           load().megamoe_packed_weight_bytes(ctypes.byref(d), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def megamoe_prepack_w1(d, w1, w1p, stream=None):
+    _check("megamoe_prepack_w1", load().megamoe_prepack_w1(
+        ctypes.byref(d), _ptr(w1, torch.int8), _ptr(w1p, torch.int8), _stream(stream)))
+
+
+def megamoe_prepack_w2(d, w2, w2p, stream=None):
+    _check("megamoe_prepack_w2", load().megamoe_prepack_w2(
+        ctypes.byref(d), _ptr(w2, torch.int8), _ptr(w2p, torch.int8), _stream(stream)))
+
+
+def megamoe_forward(d, x, expert_idx, probs, w1p, scale1, w2p, scale2, out, workspace,
+                    stream=None):
+    _check("megamoe_forward", load().megamoe_forward(
+        ctypes.byref(d), _ptr(x, torch.float16), _ptr(expert_idx, torch.int32),
+        _ptr(probs, torch.float32), _ptr(w1p, torch.int8), _ptr(scale1, torch.float32),
+        _ptr(w2p, torch.int8), _ptr(scale2, torch.float32), _ptr(out, torch.bfloat16),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def megamoe_permute(d, x, expert_idx, gmA, pts1, expanded_row_idx, sorted_route,
+                    tokens_per_expert, expert_cumsum, workspace, stream=None):
+    _check("megamoe_permute", load().megamoe_permute(
+        ctypes.byref(d), _ptr(x, torch.float16), _ptr(expert_idx, torch.int32),
+        _ptr(gmA, torch.int8), _ptr(pts1, torch.float32), _ptr(expanded_row_idx, torch.int32),
+        _ptr(sorted_route, torch.int32), _ptr(tokens_per_expert, torch.int32),
+        _ptr(expert_cumsum, torch.int32), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def megamoe_gmm1(d, gmA, expert_cumsum, w1p, scale1, gmC, acc_dbg=None, stream=None):
+    _check("megamoe_gmm1", load().megamoe_gmm1(
+        ctypes.byref(d), _ptr(gmA, torch.int8), _ptr(expert_cumsum, torch.int32),
+        _ptr(w1p, torch.int8), _ptr(scale1, torch.float32), _ptr(gmC, torch.float16),
+        _ptr(acc_dbg, torch.int32), _stream(stream)))
+
+
+def megamoe_swiglu_quant(d, gmC, pts1, expert_cumsum, q2, pts2, stream=None):
+    _check("megamoe_swiglu_quant", load().megamoe_swiglu_quant(
+        ctypes.byref(d), _ptr(gmC, torch.float16), _ptr(pts1, torch.float32),
+        _ptr(expert_cumsum, torch.int32), _ptr(q2, torch.int8), _ptr(pts2, torch.float32),
+        _stream(stream)))
+
+
+def megamoe_gmm2(d, q2, expert_cumsum, w2p, scale2, gmm2_out, acc_dbg=None, stream=None):
+    _check("megamoe_gmm2", load().megamoe_gmm2(
+        ctypes.byref(d), _ptr(q2, torch.int8), _ptr(expert_cumsum, torch.int32),
+        _ptr(w2p, torch.int8), _ptr(scale2, torch.float32), _ptr(gmm2_out, torch.float16),
+        _ptr(acc_dbg, torch.int32), _stream(stream)))
+
+
+def megamoe_unpermute(d, gmm2_out, pts2, expanded_row_idx, probs, out, stream=None):
+    _check("megamoe_unpermute", load().megamoe_unpermute(
+        ctypes.byref(d), _ptr(gmm2_out, torch.float16), _ptr(pts2, torch.float32),
+        _ptr(expanded_row_idx, torch.int32), _ptr(probs, torch.float32),
+        _ptr(out, torch.bfloat16), _stream(stream)))
+
+
+def megamoe_last_error(workspace, stream=None) -> int:
+    v = ctypes.c_int32(0)
+    _check("megamoe_last_error", load().megamoe_last_error(_ptr(workspace), _stream(stream),
+                                                           ctypes.byref(v)))
+    return v.value
+
+
+class MegaMoE:
+    """Convenience holder: packed weights + workspace for one set of dims."""
+
+    def __init__(self, M: int, K: int, E: int, top_k: int, I: int, device="cuda"):
+        self.d = dims(M, K, E, top_k, I)
+        _check("megamoe_check_dims", megamoe_check_dims(self.d))
+        self.device = torch.device(device)
+        self.workspace = torch.empty(megamoe_workspace_bytes(self.d), dtype=torch.uint8,
+                                     device=self.device)
+        n1, n2 = megamoe_packed_weight_bytes(self.d)
+        self.w1p = torch.empty(n1, dtype=torch.int8, device=self.device)
+        self.w2p = torch.empty(n2, dtype=torch.int8, device=self.device)
+        self.scale1 = None
+        self.scale2 = None
+
+    def load_weights(self, w1, scale1, w2, scale2):
+        megamoe_prepack_w1(self.d, w1, self.w1p)
+        megamoe_prepack_w2(self.d, w2, self.w2p)
+        self.scale1 = scale1.contiguous()
+        self.scale2 = scale2.contiguous()
+
+    def forward(self, x, expert_idx, probs, out=None):
+        if out is None:
+            out = torch.empty((self.d.M, self.d.K), dtype=torch.bfloat16, device=self.device)
+        megamoe_forward(self.d, x, expert_idx, probs, self.w1p, self.scale1, self.w2p,
+                        self.scale2, out, self.workspace)
+        return out
+
+    def last_error(self) -> int:
+        return megamoe_last_error(self.workspace)

@@ -1,0 +1,83 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/megamoe.h declares, and rejects bad arguments
+synchronously without touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_expert_ffn_amd import megamoe as MM
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(megamoe_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = MM.load()
+    declared = _declared()
+    assert declared, "no declarations found"
+    for n in sorted(declared):
+        assert hasattr(lib, n), f"missing export {n}"
+    assert declared == set(MM.EXPORTED)
+
+
+def test_check_dims_limits():
+    ok = MM.dims(2048, 7168, 32, 8, 2048)
+    assert MM.megamoe_check_dims(ok) == 0
+    bad = [
+        (MM.dims(0, 128, 4, 2, 128), 1),
+        (MM.dims(4, 100, 4, 2, 128), 2),      # K % 128
+        (MM.dims(4, 128, 4, 5, 128), 2),      # top_k > E
+        (MM.dims(4, 128, 300, 2, 128), 2),    # E > 256
+        (MM.dims(4, 128, 4, 2, 130), 2),      # I % 128
+        (MM.dims(1 << 20, 32768, 8, 8, 128), 2),  # R * K overflows int32
+    ]
+    for d, code in bad:
+        assert MM.megamoe_check_dims(d) == code, d
+
+
+def test_workspace_and_packed_sizes():
+    d = MM.dims(2048, 7168, 32, 8, 2048)
+    ws = MM.megamoe_workspace_bytes(d)
+    R = 2048 * 8
+    # intermediates: gmA + gmC + q2 + gmm2_out dominate
+    assert ws >= R * 7168 + R * 4096 * 2 + R * 2048 + R * 7168 * 2
+    assert ws < R * 7168 * 6
+    assert MM.megamoe_packed_weight_bytes(d) == (32 * 7168 * 4096, 32 * 2048 * 7168)
+    assert MM.megamoe_permute_workspace_bytes(d) >= 4
+    with pytest.raises(MM.MegaMoEError):
+        MM.megamoe_workspace_bytes(MM.dims(4, 100, 4, 2, 128))
+
+
+def test_null_and_misaligned_pointers_rejected():
+    lib = MM.load()
+    d = MM.dims(16, 256, 4, 2, 128)
+    P = ctypes.c_void_p
+    null = [None] * 12
+    assert lib.megamoe_forward(ctypes.byref(d), *null[:9], ctypes.c_size_t(1 << 30), None) == 1
+    odd = P(0x1000 + 4)
+    good = P(0x1000)
+    rc = lib.megamoe_unpermute(ctypes.byref(d), odd, good, good, good, good, None)
+    assert rc == 1
+    rc = lib.megamoe_gmm1(ctypes.byref(d), good, good, good, good, good, odd, None)
+    assert rc == 1
+    # workspace too small is reported before anything is launched
+    rc = lib.megamoe_forward(ctypes.byref(d), *([good] * 9), ctypes.c_size_t(16), None)
+    assert rc == 3
+
+
+def test_strerror():
+    assert MM.strerror(0) == "ok"
+    assert "workspace" in MM.strerror(3)

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Gates, per stage:
+  * sort outputs, counts, cumsum, int32 GEMM accumulators: bit-exact;
+  * gmA, q2 (int8): at most 1 LSB apart on at most 0.1% of elements;
+  * pts1 bit-exact, pts2 within 1e-6 relative;
+  * out: |out - out_ref_f32| <= 2e-2 * max|out_ref_f32|.
+gmC and gmm2_out (fp16 of an exact int32 times an fp32 scale) are expected to
+match bit for bit wherever the inputs match; that is checked too.
+
+Small shapes run the whole oracle and compare every element; they cover each
+GEMM tile variant (mean rows per expert <= 40, <= 96, <= 192, more), ragged
+N tails, empty experts, M = 1, a single hot expert and dropped routes.  The
+full workload sizes compare the sort and quantisation everywhere and the GEMM
+chain on sampled tokens the oracle evaluates one at a time.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from moe_expert_ffn_amd import inputs as W  # noqa: E402
+from moe_expert_ffn_amd import megamoe as MM  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from tests import gpu_helpers as H  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    MM.load()  # fail loudly when the HIP library is missing
+
+
+SMALL = [
+    W.WORKLOADS["tiny"],
+    W.custom(64, 384, 16, 4, 128, name="v0_mean16_raggedN"),        # BM=32 variant, N=384
+    W.custom(200, 256, 6, 2, 256, name="v1_mean67"),                # BM=64 variant
+    W.custom(333, 512, 8, 3, 128, name="v2_mean125"),               # BM=128 variant
+    W.custom(700, 256, 4, 2, 384, name="v3_mean350"),               # BM=256 variant
+    W.custom(512, 256, 16, 4, 128, routing="zipf_empty", name="zipf_empty_groups"),
+    W.custom(1, 128, 4, 2, 128, name="single_token"),
+    W.custom(96, 640, 64, 6, 256, routing="zipf", name="skew_E64"),
+]
+
+
+def _compare_full(w, inp, o_ref, g):
+    """Every intermediate of the staged GPU run against the full oracle."""
+    R = w.R
+    for k in ("sorted_route", "expanded_row_idx", "tokens_per_expert", "expert_cumsum"):
+        assert np.array_equal(g[k].cpu().numpy(), o_ref[k]), k
+    assert g["dropped"] == o_ref["dropped"]
+    Rv = R - o_ref["dropped"]
+    gmA = g["gmA"].cpu().numpy()[:Rv]
+    H.assert_int8_within_1lsb(gmA, o_ref["gmA"][:Rv], "gmA")
+    assert np.array_equal(g["pts1"].cpu().numpy()[:Rv], o_ref["pts1"][:Rv]), "pts1"
+    acc1 = g["acc1"].cpu().numpy()[:Rv]
+    assert np.array_equal(acc1, o_ref["acc1"][:Rv]), "acc1"
+    gmC = g["gmC"].cpu().numpy()[:Rv]
+    assert np.array_equal(gmC.view(np.uint16), o_ref["gmC"][:Rv].view(np.uint16)), "gmC"
+    q2 = g["q2"].cpu().numpy()[:Rv]
+    H.assert_int8_within_1lsb(q2, o_ref["q2"][:Rv], "q2")
+    p2 = g["pts2"].cpu().numpy()[:Rv]
+    np.testing.assert_allclose(p2, o_ref["pts2"][:Rv], rtol=1e-6, atol=0)
+    same_q = np.all(q2 == o_ref["q2"][:Rv], axis=1)
+    acc2 = g["acc2"].cpu().numpy()[:Rv]
+    assert np.array_equal(acc2[same_q], o_ref["acc2"][:Rv][same_q]), "acc2"
+    g2 = g["gmm2_out"].cpu().numpy()[:Rv]
+    assert np.array_equal(g2[same_q].view(np.uint16),
+                          o_ref["gmm2_out"][:Rv][same_q].view(np.uint16)), "gmm2_out"
+    H.assert_out_close(H.bf16_f32(g["out"]), o_ref["out_f32"])
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_stages_and_forward_small(w):
+    print(f"[parity] {w.describe()}", flush=True)
+    inp = W.generate(w, seed=0)
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    # the fused forward equals the staged run bit for bit
+    out, dropped = H.run_forward(w, dev, w1p, w2p)
+    assert dropped == o_ref["dropped"]
+    assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
+
+
+def test_hot_expert_and_duplicates():
+    # every token sends both slots to expert 5: one group of 2M rows
+    w = W.custom(300, 256, 8, 2, 128, name="hot_expert")
+    inp = W.generate(w, seed=1)
+    inp["expert_idx"][:] = 5
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+
+
+def test_dropped_routes_error_word():
+    w = W.custom(40, 256, 8, 3, 128, name="dropped")
+    inp = W.generate(w, seed=2)
+    inp["expert_idx"][3, 1] = 8        # == E: out of range
+    inp["expert_idx"][7, 0] = -1
+    inp["expert_idx"][39, 2] = 1000
+    o_ref = O.forward(inp)
+    assert o_ref["dropped"] == 3
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    assert g["dropped"] == 3
+    _compare_full(w, inp, o_ref, g)
+    # the error word is reset by the next call
+    inp2 = W.generate(w, seed=2)
+    dev2 = H.to_dev(inp2)
+    out, dropped = H.run_forward(w, dev2, w1p, w2p)
+    assert dropped == 0
+
+
+def test_repeat_launch_bit_identical():
+    w = W.custom(257, 512, 16, 4, 256, routing="zipf", name="determinism")
+    inp = W.generate(w, seed=4)
+    dev = H.to_dev(inp)
+    d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
+    w1p, w2p = H.prepack(d, dev)
+    ws = torch.empty(MM.megamoe_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(6):
+        out = torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda")
+        MM.megamoe_forward(d, dev["x"], dev["expert_idx"], dev["probs"], w1p, dev["scale1"],
+                           w2p, dev["scale2"], out, ws)
+        outs.append(H.bf16_bits(out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes: sort / quant everywhere, sampled tokens for the GEMMs
+# ----------------------------------------------------------------------------
+FULL = ["decode", "mid", "large", "skewed", "skewed_empty"]
+
+
+def _sample_tokens(M: int, n: int, seed: int) -> list[int]:
+    rng = np.random.default_rng(seed)
+    picks = {0, M - 1}
+    picks.update(int(t) for t in rng.choice(M, size=min(n, M), replace=False))
+    return sorted(picks)[: n + 2]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    w = W.WORKLOADS[name]
+    print(f"[parity-full] {w.describe()}", flush=True)
+    inp = W.generate(w, seed=0)
+    dev = H.to_dev(inp)
+    d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
+    w1p, w2p = H.prepack(d, dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    out_fwd, dropped = H.run_forward(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    assert dropped == 0 and g["dropped"] == 0
+    # the forward (timed by the benchmark) equals the staged run
+    assert np.array_equal(H.bf16_bits(out_fwd), H.bf16_bits(g["out"]))
+
+    # sort metadata: bit-exact everywhere
+    srt = O.route_sort(inp["expert_idx"], w.E)
+    for k in ("sorted_route", "expanded_row_idx", "tokens_per_expert", "expert_cumsum"):
+        assert np.array_equal(g[k].cpu().numpy(), srt[k]), k
+    eri = srt["expanded_row_idx"]
+
+    # quantisation: every token
+    gmA = g["gmA"].cpu().numpy()
+    pts1 = g["pts1"].cpu().numpy()
+    q_ref = np.empty((w.M, w.K), np.int8)
+    s_ref = np.empty(w.M, np.float32)
+    for t in range(w.M):
+        q_ref[t], s_ref[t] = O.quant_token(inp["x"][t])
+    rows = eri.reshape(w.M, w.top_k)
+    H.assert_int8_within_1lsb(gmA[rows.ravel()], np.repeat(q_ref, w.top_k, axis=0), "gmA")
+    assert np.array_equal(pts1[rows.ravel()], np.repeat(s_ref, w.top_k)), "pts1"
+
+    # sampled tokens through the oracle's per-token forward
+    acc1 = g["acc1"]
+    acc2 = g["acc2"]
+    q2_bad = 0
+    q2_total = 0
+    out_gpu = H.bf16_f32(g["out"])
+    errs = []
+    ref_rows = []
+    got_rows = []
+    for t in _sample_tokens(w.M, 6, seed=1):
+        ot = O.forward_token(inp, t)
+        for s in range(w.top_k):
+            dr = int(rows[t, s])
+            assert np.array_equal(acc1[dr].cpu().numpy(), ot["acc1"][s]), f"acc1 t={t} s={s}"
+            assert np.array_equal(g["gmC"][dr].cpu().numpy().view(np.uint16),
+                                  ot["gmC"][s].view(np.uint16)), f"gmC t={t} s={s}"
+            q2g = g["q2"][dr].cpu().numpy()
+            diff = np.abs(q2g.astype(int) - ot["q2"][s].astype(int))
+            assert diff.max() <= 1
+            q2_bad += int(np.count_nonzero(diff))
+            q2_total += diff.size
+            np.testing.assert_allclose(g["pts2"][dr].item(), ot["pts2"][s], rtol=1e-6)
+            if not diff.any():
+                assert np.array_equal(acc2[dr].cpu().numpy(), ot["acc2"][s]), f"acc2 t={t}"
+        ref_rows.append(ot["out_f32"])
+        got_rows.append(out_gpu[t])
+    assert q2_bad <= 1e-3 * q2_total, f"q2: {q2_bad}/{q2_total} differ"
+    H.assert_out_close(np.stack(got_rows), np.stack(ref_rows))
+    # properties that hold at any size
+    assert np.all(np.isfinite(out_gpu))
+    cnt = g["tokens_per_expert"].cpu().numpy()
+    assert cnt.sum() == w.R
+    if name == "skewed_empty":
+        assert np.all(cnt[48:] == 0)
