@@ -33,56 +33,72 @@ __device__ __forceinline__ uint64_t match_key(int key, uint64_t valid, int nbits
     return m;
 }
 
-// One workgroup.  Wave w owns a contiguous run of 64-route chunks, so route
-// order is preserved: all of wave w's routes precede wave w+1's.
+// One workgroup.  The expert ids are first copied to LDS in segments of up to
+// kSegRoutes routes (all loads in flight at once), then every pass reads LDS.
+// Within a segment, wave w owns a contiguous run of 64-route chunks, so route
+// order is preserved: segment s precedes s+1, and inside a segment wave w's
+// routes precede wave w+1's.
+constexpr int kSegRoutes = 32768;
+
+__device__ __forceinline__ void load_keys(const int32_t *__restrict__ expert_idx, int r0, int n,
+                                          int E, int16_t *keys) {
+    for (int i = threadIdx.x; i < n; i += kSortThreads) {
+        const int e = expert_idx[r0 + i];
+        keys[i] = (int16_t)((e >= 0 && e < E) ? e : E);  // E marks a dropped route
+    }
+}
+
+// Per-wave key counts of one segment into cnt[wave][*] (zeroed by the caller).
+__device__ __forceinline__ void count_segment(const int16_t *keys, int n, int E, int nbits,
+                                              int (*cnt)[kMaxExperts]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int nchunks = (n + kWave - 1) / kWave;
+    const int c_begin = (int)((int64_t)nchunks * wave / kSortWaves);
+    const int c_end = (int)((int64_t)nchunks * (wave + 1) / kSortWaves);
+    for (int c = c_begin; c < c_end; ++c) {
+        const int i = c * kWave + lane;
+        const int key = (i < n) ? keys[i] : E;
+        const bool ok = key < E;
+        const uint64_t m = match_key(key, __ballot(ok), nbits);
+        if (ok && (m & below) == 0) cnt[wave][key] += __popcll(m);
+    }
+}
+
 __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
     const int32_t *__restrict__ expert_idx, int R, int E, int nbits,
     int32_t *__restrict__ sorted_route, int32_t *__restrict__ expanded_row_idx,
     int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_cumsum,
     int32_t *__restrict__ err_word) {
-    __shared__ int cnt[kSortWaves][kMaxExperts];  // per-wave histogram, then row bases
+    __shared__ int cnt[kSortWaves][kMaxExperts];  // per-wave counts, then row bases
     __shared__ int s_total[kMaxExperts];
-    __shared__ int s_off[kMaxExperts];
+    __shared__ int s_run[kMaxExperts];            // next free row of each expert
     __shared__ int s_valid;
+    __shared__ int16_t keys[kSegRoutes];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid >> 6;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int nseg = (R + kSegRoutes - 1) / kSegRoutes;
 
-    for (int i = tid; i < kSortWaves * kMaxExperts; i += kSortThreads) (&cnt[0][0])[i] = 0;
-    __syncthreads();
-
-    const int nchunks = (R + kWave - 1) / kWave;
-    const int c_begin = (int)((int64_t)nchunks * wave / kSortWaves);
-    const int c_end = (int)((int64_t)nchunks * (wave + 1) / kSortWaves);
-
-    // Pass 1: per-wave counts.
-    for (int c = c_begin; c < c_end; ++c) {
-        const int r = c * kWave + lane;
-        int key = E;  // E = "dropped" (out of range or past the end)
-        if (r < R) {
-            const int e = expert_idx[r];
-            key = (e >= 0 && e < E) ? e : E;
+    if (tid < kMaxExperts) s_total[tid] = 0;
+    // Pass A: totals per expert.
+    for (int sgi = 0; sgi < nseg; ++sgi) {
+        const int r0 = sgi * kSegRoutes, n = min(kSegRoutes, R - r0);
+        for (int i = tid; i < kSortWaves * kMaxExperts; i += kSortThreads) (&cnt[0][0])[i] = 0;
+        load_keys(expert_idx, r0, n, E, keys);
+        __syncthreads();
+        count_segment(keys, n, E, nbits, cnt);
+        __syncthreads();
+        if (tid < E) {
+            int v = 0;
+            for (int w = 0; w < kSortWaves; ++w) v += cnt[w][tid];
+            s_total[tid] += v;
         }
-        const uint64_t valid = __ballot(r < R && key < E);
-        const uint64_t m = match_key(key, valid, nbits);
-        const bool leader = (r < R) && (key < E) && ((m & below) == 0);
-        if (leader) cnt[wave][key] += __popcll(m);
+        __syncthreads();
     }
-    __syncthreads();
-
-    // Per expert: totals and exclusive prefix over waves.
-    if (tid < E) {
-        int run = 0;
-        for (int w = 0; w < kSortWaves; ++w) {
-            const int v = cnt[w][tid];
-            cnt[w][tid] = run;
-            run += v;
-        }
-        s_total[tid] = run;
-    }
-    __syncthreads();
 
     // Exclusive prefix over experts (wave 0, four experts per lane).
     if (wave == 0) {
@@ -99,45 +115,61 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane * 4 + j;
-            if (e < E) s_off[e] = run;
+            if (e < E) s_run[e] = run;
             run += v[j];
         }
         if (lane == kWave - 1) s_valid = incl;
     }
     __syncthreads();
-
     if (tid < E) {
-        const int off = s_off[tid];
-        for (int w = 0; w < kSortWaves; ++w) cnt[w][tid] += off;
         tokens_per_expert[tid] = s_total[tid];
-        expert_cumsum[tid] = off + s_total[tid];
+        expert_cumsum[tid] = s_run[tid] + s_total[tid];
     }
     const int valid_rows = s_valid;
     if (tid == 0) err_word[0] = R - valid_rows;
-    __syncthreads();
 
-    // Pass 2: stable destination rows.
-    for (int c = c_begin; c < c_end; ++c) {
-        const int r = c * kWave + lane;
-        int key = E;
-        if (r < R) {
-            const int e = expert_idx[r];
-            key = (e >= 0 && e < E) ? e : E;
+    // Pass B: stable destination rows, segment by segment.
+    for (int sgi = 0; sgi < nseg; ++sgi) {
+        const int r0 = sgi * kSegRoutes, n = min(kSegRoutes, R - r0);
+        if (nseg > 1) {  // a single segment still holds its keys and counts
+            __syncthreads();
+            for (int i = tid; i < kSortWaves * kMaxExperts; i += kSortThreads)
+                (&cnt[0][0])[i] = 0;
+            load_keys(expert_idx, r0, n, E, keys);
+            __syncthreads();
+            count_segment(keys, n, E, nbits, cnt);
         }
-        const bool ok = (r < R) && (key < E);
-        const uint64_t valid = __ballot(ok);
-        const uint64_t m = match_key(key, valid, nbits);
-        const int rank = __popcll(m & below);
-        int dst = -1;
-        int base = 0;
-        if (ok) {
-            base = cnt[wave][key];
-            dst = base + rank;
+        __syncthreads();
+        // per-wave row bases of this segment
+        if (tid < E) {
+            int run = s_run[tid];
+            for (int w = 0; w < kSortWaves; ++w) {
+                const int v = cnt[w][tid];
+                cnt[w][tid] = run;
+                run += v;
+            }
+            s_run[tid] = run;
         }
-        if (ok && rank == 0) cnt[wave][key] = base + __popcll(m);
-        if (r < R) {
-            expanded_row_idx[r] = dst;
-            if (dst >= 0) sorted_route[dst] = r;
+        __syncthreads();
+        const int nchunks = (n + kWave - 1) / kWave;
+        const int c_begin = (int)((int64_t)nchunks * wave / kSortWaves);
+        const int c_end = (int)((int64_t)nchunks * (wave + 1) / kSortWaves);
+        for (int c = c_begin; c < c_end; ++c) {
+            const int i = c * kWave + lane;
+            const int key = (i < n) ? keys[i] : E;
+            const bool ok = key < E;
+            const uint64_t m = match_key(key, __ballot(ok), nbits);
+            const int rank = __popcll(m & below);
+            int dst = -1, base = 0;
+            if (ok) {
+                base = cnt[wave][key];
+                dst = base + rank;
+            }
+            if (ok && rank == 0) cnt[wave][key] = base + __popcll(m);
+            if (i < n) {
+                expanded_row_idx[r0 + i] = dst;
+                if (dst >= 0) sorted_route[dst] = r0 + i;
+            }
         }
     }
     for (int d = valid_rows + tid; d < R; d += kSortThreads) sorted_route[d] = -1;

@@ -45,6 +45,7 @@ SMALL = [
     W.custom(512, 256, 16, 4, 128, routing="zipf_empty", name="zipf_empty_groups"),
     W.custom(1, 128, 4, 2, 128, name="single_token"),
     W.custom(96, 640, 64, 6, 256, routing="zipf", name="skew_E64"),
+    W.custom(6000, 128, 64, 6, 128, routing="zipf", name="two_sort_segments"),  # R > 32768
 ]
 
 
