@@ -16,9 +16,12 @@ struct GmmParams {
     int E, N, Kred;
 };
 
+// block_counts: device scratch of route_sort_workspace_bytes(R, E) bytes
+size_t route_sort_workspace_bytes(int R, int E);
 hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *sorted_route,
                              int32_t *expanded_row_idx, int32_t *tokens_per_expert,
-                             int32_t *expert_cumsum, int32_t *err_word, hipStream_t stream);
+                             int32_t *expert_cumsum, int32_t *err_word, int32_t *block_counts,
+                             hipStream_t stream);
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
                                 int top_k, int8_t *gmA, float *pts1, hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,

@@ -35,14 +35,20 @@ int cu_count_current() {
 }
 
 struct Layout {
-    size_t err, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2, g2, total;
+    size_t err, bcnt, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2, g2, total;
 };
+
+// permute workspace: error word, then the sort's per-block expert counts
+size_t permute_ws_bytes(const megamoe_dims &d) {
+    return align_up(kErrBytes) + align_up(route_sort_workspace_bytes(d.M * d.top_k, d.E));
+}
 
 Layout forward_layout(const megamoe_dims &d) {
     const size_t R = (size_t)d.M * d.top_k;
     Layout L;
     size_t o = 0;
     L.err = o;    o += align_up(kErrBytes);
+    L.bcnt = o;   o += align_up(route_sort_workspace_bytes((int)R, d.E));
     L.eri = o;    o += align_up(R * 4);
     L.sorted = o; o += align_up(R * 4);
     L.counts = o; o += align_up((size_t)d.E * 4);
@@ -67,10 +73,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_EHI
 
 int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_idx, int8_t *gmA,
                 float *pts1, int32_t *eri, int32_t *sorted, int32_t *counts, int32_t *cumsum,
-                int32_t *err_word, hipStream_t s) {
+                int32_t *err_word, int32_t *block_counts, hipStream_t s) {
     const int R = d.M * d.top_k;
     MEGAMOE_TRY(hip_status(launch_route_sort(expert_idx, R, d.E, sorted, eri, counts, cumsum,
-                                             err_word, s)));
+                                             err_word, block_counts, s)));
     return hip_status(launch_quant_scatter(x, eri, d.M, d.K, d.top_k, gmA, pts1, s));
 }
 
@@ -118,7 +124,7 @@ int megamoe_workspace_bytes(const megamoe_dims *d, size_t *bytes) {
 int megamoe_permute_workspace_bytes(const megamoe_dims *d, size_t *bytes) {
     MEGAMOE_TRY(megamoe_check_dims(d));
     if (!bytes) return MEGAMOE_EINVAL;
-    *bytes = kErrBytes;
+    *bytes = permute_ws_bytes(*d);
     return MEGAMOE_OK;
 }
 
@@ -151,9 +157,10 @@ int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
                           expert_cumsum, ws};
     for (const void *p : ptrs)
         if (!aligned16(p)) return MEGAMOE_EINVAL;
-    if (ws_bytes < kErrBytes) return MEGAMOE_EWORKSPACE;
+    if (ws_bytes < permute_ws_bytes(*d)) return MEGAMOE_EWORKSPACE;
     return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
-                       expert_cumsum, (int32_t *)ws, (hipStream_t)stream);
+                       expert_cumsum, (int32_t *)ws, (int32_t *)((char *)ws + align_up(kErrBytes)),
+                       (hipStream_t)stream);
 }
 
 int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert_cumsum,
@@ -224,7 +231,9 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     int8_t *q2 = (int8_t *)(base + L.q2);
     uint16_t *g2 = (uint16_t *)(base + L.g2);
 
-    MEGAMOE_TRY(run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, s));
+    int32_t *bcnt = (int32_t *)(base + L.bcnt);
+    MEGAMOE_TRY(
+        run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, bcnt, s));
     MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s));
     MEGAMOE_TRY(hip_status(
         launch_swiglu_quant(gmC, pts1, cumsum, d->M * d->top_k, d->E, d->I, q2, pts2, s)));

@@ -10,16 +10,16 @@
 //
 // The page sorts with merge-sort instructions sized to its 192 KiB buffer.
 // With at most 256 expert keys a counting sort reaches the same stable order
-// with two passes over the routes: one workgroup, per-wave LDS histograms,
-// wave-ballot peer matching for in-wave ranks.
+// in two passes spread over many workgroups: per-block histograms, then per
+// block row bases and wave-ballot peer matching for the ranks inside a block.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace megamoe {
 
-constexpr int kSortThreads = 1024;
-constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kMaxExperts = 256;
+constexpr int kSortBlock = 256;          // threads per sort workgroup (4 waves)
+constexpr int kSortWavesB = kSortBlock / kWave;
 
 // Lanes of the wave holding the same key as this lane (among `valid` lanes).
 // key < 2^nbits.  One ballot per key bit.
@@ -33,81 +33,77 @@ __device__ __forceinline__ uint64_t match_key(int key, uint64_t valid, int nbits
     return m;
 }
 
-// One workgroup.  The expert ids are first copied to LDS in segments of up to
-// kSegRoutes routes (all loads in flight at once), then every pass reads LDS.
-// Within a segment, wave w owns a contiguous run of 64-route chunks, so route
-// order is preserved: segment s precedes s+1, and inside a segment wave w's
-// routes precede wave w+1's.
-constexpr int kSegRoutes = 32768;
-
-__device__ __forceinline__ void load_keys(const int32_t *__restrict__ expert_idx, int r0, int n,
-                                          int E, int16_t *keys) {
-    for (int i = threadIdx.x; i < n; i += kSortThreads) {
-        const int e = expert_idx[r0 + i];
-        keys[i] = (int16_t)((e >= 0 && e < E) ? e : E);  // E marks a dropped route
-    }
+__device__ __forceinline__ int route_key(const int32_t *__restrict__ expert_idx, int r, int R,
+                                         int E) {
+    if (r >= R) return E;
+    const int e = expert_idx[r];
+    return (e >= 0 && e < E) ? e : E;  // E marks a dropped route
 }
 
-// Per-wave key counts of one segment into cnt[wave][*] (zeroed by the caller).
-__device__ __forceinline__ void count_segment(const int16_t *keys, int n, int E, int nbits,
-                                              int (*cnt)[kMaxExperts]) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x >> 6;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    const int nchunks = (n + kWave - 1) / kWave;
-    const int c_begin = (int)((int64_t)nchunks * wave / kSortWaves);
-    const int c_end = (int)((int64_t)nchunks * (wave + 1) / kSortWaves);
-    for (int c = c_begin; c < c_end; ++c) {
-        const int i = c * kWave + lane;
-        const int key = (i < n) ? keys[i] : E;
-        const bool ok = key < E;
-        const uint64_t m = match_key(key, __ballot(ok), nbits);
-        if (ok && (m & below) == 0) cnt[wave][key] += __popcll(m);
+// Pass 1: histogram of the expert ids of routes [b*C, (b+1)*C) per block.
+// Counting is order-free, so LDS atomics are fine here.
+__global__ __launch_bounds__(kSortBlock) void route_count_kernel(
+    const int32_t *__restrict__ expert_idx, int R, int E, int C,
+    int32_t *__restrict__ block_counts /*[B][E]*/) {
+    __shared__ int h[kMaxExperts];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < E; i += kSortBlock) h[i] = 0;
+    __syncthreads();
+    const int r0 = blockIdx.x * C;
+    const int r1 = min(R, r0 + C);
+    for (int r = r0 + tid; r < r1; r += kSortBlock) {
+        const int key = route_key(expert_idx, r, R, E);
+        if (key < E) atomicAdd(&h[key], 1);
     }
+    __syncthreads();
+    for (int i = tid; i < E; i += kSortBlock) block_counts[(size_t)blockIdx.x * E + i] = h[i];
 }
 
-__global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
-    const int32_t *__restrict__ expert_idx, int R, int E, int nbits,
-    int32_t *__restrict__ sorted_route, int32_t *__restrict__ expanded_row_idx,
-    int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_cumsum,
-    int32_t *__restrict__ err_word) {
-    __shared__ int cnt[kSortWaves][kMaxExperts];  // per-wave counts, then row bases
-    __shared__ int s_total[kMaxExperts];
-    __shared__ int s_run[kMaxExperts];            // next free row of each expert
+// Pass 2: each block derives the first row of every expert for its routes
+// (exclusive prefix over experts of the totals, plus the counts of the blocks
+// before it), then ranks its routes in route order: 256 routes per round, one
+// 64-route chunk per wave, ranks inside a wave from ballot peer matching, the
+// waves ordered by their per-expert counts.  Block 0 also writes the counts,
+// the inclusive prefix and the dropped-route word.
+__global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
+    const int32_t *__restrict__ expert_idx, int R, int E, int C, int nbits, int B,
+    const int32_t *__restrict__ block_counts, int32_t *__restrict__ sorted_route,
+    int32_t *__restrict__ expanded_row_idx, int32_t *__restrict__ tokens_per_expert,
+    int32_t *__restrict__ expert_cumsum, int32_t *__restrict__ err_word) {
+    __shared__ int s_base[kMaxExperts];   // next row of each expert for this block
+    __shared__ int s_tot[kMaxExperts];
+    __shared__ int s_wcnt[kSortWavesB][kMaxExperts];
     __shared__ int s_valid;
-    __shared__ int16_t keys[kSegRoutes];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid >> 6;
+    const int b = blockIdx.x;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    const int nseg = (R + kSegRoutes - 1) / kSegRoutes;
 
-    if (tid < kMaxExperts) s_total[tid] = 0;
-    // Pass A: totals per expert.
-    for (int sgi = 0; sgi < nseg; ++sgi) {
-        const int r0 = sgi * kSegRoutes, n = min(kSegRoutes, R - r0);
-        for (int i = tid; i < kSortWaves * kMaxExperts; i += kSortThreads) (&cnt[0][0])[i] = 0;
-        load_keys(expert_idx, r0, n, E, keys);
-        __syncthreads();
-        count_segment(keys, n, E, nbits, cnt);
-        __syncthreads();
-        if (tid < E) {
-            int v = 0;
-            for (int w = 0; w < kSortWaves; ++w) v += cnt[w][tid];
-            s_total[tid] += v;
-        }
-        __syncthreads();
+    for (int e = tid; e < E; e += kSortBlock) {
+        s_tot[e] = 0;
+        s_base[e] = 0;
     }
-
-    // Exclusive prefix over experts (wave 0, four experts per lane).
-    if (wave == 0) {
+    __syncthreads();
+    // all (block, expert) entries of the table, coalesced; integer sums are
+    // order-free, so LDS atomics accumulate them
+    for (int i = tid; i < B * E; i += kSortBlock) {
+        const int bb = i / E, e = i - bb * E;
+        const int v = block_counts[i];
+        if (v) {
+            atomicAdd(&s_tot[e], v);
+            if (bb < b) atomicAdd(&s_base[e], v);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive prefix of the totals over experts, four per lane
         int v[4];
         int sum = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane * 4 + j;
-            v[j] = (e < E) ? s_total[e] : 0;
+            v[j] = (e < E) ? s_tot[e] : 0;
             sum += v[j];
         }
         const int incl = wave_inclusive_scan(sum);
@@ -115,64 +111,54 @@ __global__ __launch_bounds__(kSortThreads) void route_sort_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane * 4 + j;
-            if (e < E) s_run[e] = run;
+            if (e < E) {
+                if (b == 0) {
+                    tokens_per_expert[e] = v[j];
+                    expert_cumsum[e] = run + v[j];
+                }
+                s_base[e] += run;
+            }
             run += v[j];
         }
         if (lane == kWave - 1) s_valid = incl;
     }
     __syncthreads();
-    if (tid < E) {
-        tokens_per_expert[tid] = s_total[tid];
-        expert_cumsum[tid] = s_run[tid] + s_total[tid];
-    }
     const int valid_rows = s_valid;
-    if (tid == 0) err_word[0] = R - valid_rows;
-
-    // Pass B: stable destination rows, segment by segment.
-    for (int sgi = 0; sgi < nseg; ++sgi) {
-        const int r0 = sgi * kSegRoutes, n = min(kSegRoutes, R - r0);
-        if (nseg > 1) {  // a single segment still holds its keys and counts
-            __syncthreads();
-            for (int i = tid; i < kSortWaves * kMaxExperts; i += kSortThreads)
-                (&cnt[0][0])[i] = 0;
-            load_keys(expert_idx, r0, n, E, keys);
-            __syncthreads();
-            count_segment(keys, n, E, nbits, cnt);
-        }
-        __syncthreads();
-        // per-wave row bases of this segment
-        if (tid < E) {
-            int run = s_run[tid];
-            for (int w = 0; w < kSortWaves; ++w) {
-                const int v = cnt[w][tid];
-                cnt[w][tid] = run;
-                run += v;
-            }
-            s_run[tid] = run;
-        }
-        __syncthreads();
-        const int nchunks = (n + kWave - 1) / kWave;
-        const int c_begin = (int)((int64_t)nchunks * wave / kSortWaves);
-        const int c_end = (int)((int64_t)nchunks * (wave + 1) / kSortWaves);
-        for (int c = c_begin; c < c_end; ++c) {
-            const int i = c * kWave + lane;
-            const int key = (i < n) ? keys[i] : E;
-            const bool ok = key < E;
-            const uint64_t m = match_key(key, __ballot(ok), nbits);
-            const int rank = __popcll(m & below);
-            int dst = -1, base = 0;
-            if (ok) {
-                base = cnt[wave][key];
-                dst = base + rank;
-            }
-            if (ok && rank == 0) cnt[wave][key] = base + __popcll(m);
-            if (i < n) {
-                expanded_row_idx[r0 + i] = dst;
-                if (dst >= 0) sorted_route[dst] = r0 + i;
-            }
-        }
+    if (b == 0) {
+        if (tid == 0) err_word[0] = R - valid_rows;
+        for (int d = valid_rows + tid; d < R; d += kSortBlock) sorted_route[d] = -1;
     }
-    for (int d = valid_rows + tid; d < R; d += kSortThreads) sorted_route[d] = -1;
+
+    const int r_end = min(R, (b + 1) * C);
+    for (int r0 = b * C; r0 < r_end; r0 += kSortBlock) {
+        for (int i = tid; i < kSortWavesB * kMaxExperts; i += kSortBlock) (&s_wcnt[0][0])[i] = 0;
+        __syncthreads();
+        const int r = r0 + wave * kWave + lane;
+        const int key = (r < r_end) ? route_key(expert_idx, r, R, E) : E;
+        const bool ok = key < E;
+        const uint64_t m = match_key(key, __ballot(ok), nbits);
+        const int rank = __popcll(m & below);
+        if (ok && rank == 0) s_wcnt[wave][key] = __popcll(m);
+        __syncthreads();
+        int dst = -1;
+        if (ok) {
+            int pre = s_base[key];
+            for (int w = 0; w < wave; ++w) pre += s_wcnt[w][key];
+            dst = pre + rank;
+        }
+        if (r < r_end) {
+            expanded_row_idx[r] = dst;
+            if (dst >= 0) sorted_route[dst] = r;
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += kSortBlock) {
+            int add = 0;
+            for (int w = 0; w < kSortWavesB; ++w) add += s_wcnt[w][e];
+            s_base[e] += add;
+        }
+        // the next round's zeroing is ordered after these reads by its barrier
+        __syncthreads();
+    }
 }
 
 // One workgroup per token.  Each thread owns 16-element chunks of the row
@@ -247,14 +233,34 @@ __global__ __launch_bounds__(256) void quant_scatter_kernel(
     }
 }
 
+// Routes per sort block: at least 256, and at most 256 blocks so that each
+// block's pass over the block-count table stays short.
+int route_sort_chunk(int R) {
+    const int per = (R + 255) / 256;
+    return max(kSortBlock, (per + kSortBlock - 1) / kSortBlock * kSortBlock);
+}
+
+size_t route_sort_workspace_bytes(int R, int E) {
+    const int C = route_sort_chunk(R);
+    const int B = (R + C - 1) / C;
+    return (size_t)B * E * sizeof(int32_t);
+}
+
 hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *sorted_route,
                              int32_t *expanded_row_idx, int32_t *tokens_per_expert,
-                             int32_t *expert_cumsum, int32_t *err_word, hipStream_t stream) {
+                             int32_t *expert_cumsum, int32_t *err_word, int32_t *block_counts,
+                             hipStream_t stream) {
     int nbits = 0;
     while ((1 << nbits) <= E) ++nbits;  // keys 0..E (E = dropped)
-    hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(kSortThreads), 0, stream, expert_idx, R,
-                       E, nbits, sorted_route, expanded_row_idx, tokens_per_expert, expert_cumsum,
-                       err_word);
+    const int C = route_sort_chunk(R);
+    const int B = (R + C - 1) / C;
+    hipLaunchKernelGGL(route_count_kernel, dim3(B), dim3(kSortBlock), 0, stream, expert_idx, R, E,
+                       C, block_counts);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(B), dim3(kSortBlock), 0, stream, expert_idx, R,
+                       E, C, nbits, B, block_counts, sorted_route, expanded_row_idx,
+                       tokens_per_expert, expert_cumsum, err_word);
     return hipGetLastError();
 }
 
