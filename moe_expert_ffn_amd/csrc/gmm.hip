@@ -38,8 +38,8 @@ constexpr int kMaxE = 256;
 // ---------------------------------------------------------------------------
 // Deeper pipeline: 64-byte K stages, each thread keeps the next D stages of its
 // A/B chunks in flight in registers while the LDS double buffer feeds the MFMAs.
-// LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot c ^ ((r >> 2) & 3)
-// so the 16 rows of a fragment read cover all banks once.
+// LDS rows are 64 bytes; 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 3),
+// the conflict-free pattern for the fragment reads.
 // ---------------------------------------------------------------------------
 constexpr int kBK64 = 64;
 
@@ -52,7 +52,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 }
 
 __device__ __forceinline__ int lds_off64(int row, int chunk) {
-    return row * kBK64 + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+    return row * kBK64 + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
 
 // Builds the per-expert tile prefix in LDS (wave 0) and returns the tile count.
@@ -83,6 +83,43 @@ __device__ __forceinline__ int build_tile_prefix(const GmmParams &p, int NB, int
     }
     __syncthreads();
     return s_tile_start[p.E];
+}
+
+// The MFMAs compute the transposed tile (weight fragment as the first operand,
+// activation fragment as the second), so in the 16x16 result of fragment
+// (i, j) lane l holds output row 16 i + (l & 15) and the 4 consecutive output
+// columns 16 j + 4 (l >> 4) + v, v = 0..3.  The store is then one 8-byte fp16
+// quad per lane (the per-channel scales one float4), and the 4 lane groups of
+// a row write 32 contiguous bytes.
+__device__ __forceinline__ v4i mfma_t(const v4i &b_frag, const v4i &a_frag, const v4i &acc) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(b_frag, a_frag, acc, 0, 0, 0);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile(const GmmParams &p, const v4i (&acc)[TM][TN], int e,
+                                           int row0, int rows, int n0, int wm0, int wn0,
+                                           int lane) {
+    const int N = p.N;
+    const float *sc = p.scale + (size_t)e * N;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn0 + 16 * j + 4 * (lane >> 4);
+        if (col >= N) continue;  // N is a multiple of 16, so col + 3 < N here
+        const float4 s4 = *reinterpret_cast<const float4 *>(sc + col);
+        const float s[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int rl = wm0 + 16 * i + (lane & 15);
+            if (rl >= rows) continue;
+            const size_t idx = (size_t)(row0 + rl) * N + col;
+            uint32_t h[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) h[v] = f2h(keep_f32((float)acc[i][j][v] * s[v]));
+            *reinterpret_cast<uint2 *>(p.C + idx) =
+                make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            if (p.acc_dbg) *reinterpret_cast<v4i *>(p.acc_dbg + idx) = acc[i][j];
+        }
+    }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int D>
@@ -222,8 +259,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_pipe_kernel(Gm
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j],
-                                                                              acc[i][j], 0, 0, 0);
+                            acc[i][j] = mfma_t(fb[j], fa[i], acc[i][j]);
                 }
                 int8_t *sn = smem[(kt + 1) & 1];
 #pragma unroll
@@ -236,26 +272,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_pipe_kernel(Gm
             });
         }
 
-        const float *sc = p.scale + (size_t)e * N;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn0 + 16 * j + (lane & 15);
-            if (col >= N) continue;
-            const float s = sc[col];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int rl = wm0 + 16 * i + 4 * (lane >> 4) + v;
-                    if (rl < rows) {
-                        const size_t idx = (size_t)(row0 + rl) * N + col;
-                        const int a = acc[i][j][v];
-                        p.C[idx] = f2h(keep_f32((float)a * s));
-                        if (p.acc_dbg) p.acc_dbg[idx] = a;
-                    }
-                }
-            }
-        }
+        store_tile<TM, TN>(p, acc, e, row0, rows, n0, wm0, wn0, lane);
     }
 }
 
@@ -269,12 +286,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_pipe_kernel(Gm
 // at most (NS - 2) stages of its DMA are outstanding; a barrier then makes all
 // waves' chunks visible.
 //
-// Layout: 64-byte rows; 16-byte chunk c of row r sits at slot
-// c ^ (((r >> 1) ^ (r >> 3)) & 3).  Any 8 consecutive rows (one 128-byte bank
-// sweep) and any 16 consecutive rows read with one chunk index hit distinct
-// bank groups, for both reads and DMA writes.
+// Layout: 64-byte rows; 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 3).
+// Measured with the LDS bank-conflict counter on gfx950, this is the pattern
+// for which the fragment reads (16 consecutive rows, one chunk index per lane
+// group) see no conflicts.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz64(int row) { return (row >> 1) & 3; }
 __device__ __forceinline__ int lds_off64s(int row, int chunk) {
     return row * kBK64 + ((chunk ^ swz64(row)) << 4);
 }
@@ -412,33 +429,264 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_dma_kernel(Gmm
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0,
-                                                                      0, 0);
+                    acc[i][j] = mfma_t(fb[j], fa[i], acc[i][j]);
         }
         // drain the prefetches past the end before the ring is reused
         wait_vmcnt<0>();
         __syncthreads();
 
-        const float *sc = p.scale + (size_t)e * N;
+        store_tile<TM, TN>(p, acc, e, row0, rows, n0, wm0, wn0, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Shifted DMA pipeline with register double-buffered fragments.
+//
+// A stage is S sub-steps of 64 K-bytes ([S][BM + BN rows][64 B], swizzled as
+// above), copied by DMA into an NS-deep ring (NS >= 3).  Fragments for the
+// next sub-step are read from LDS while the MFMAs of the current one run.  The
+// barrier that publishes stage kt+1 sits right before the prefetch of its first
+// sub-step, i.e. at the start of the last sub-step of stage kt; the DMA of
+// stage kt+NS-1 is issued right after it, into the slot of stage kt-1 (whose
+// last fragments were read before that barrier).  Stage kt+1 was issued NS-2
+// stages earlier, so at the barrier NS-3 stages may still be in flight.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WAVES_M, int WAVES_N, int S, int NS>
+__global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
+    constexpr int NW = WAVES_M * WAVES_N;
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 16, TN = WN / 16;
+    constexpr int kSub = (BM + BN) * kBK64;          // bytes of one 64-byte K slice
+    constexpr int kStage = kSub * S;
+    constexpr int kBlocks = kStage / 1024;
+    constexpr int LPW = kBlocks / NW;
+    static_assert(kSub % 1024 == 0 && kBlocks % NW == 0, "stage must split over the waves");
+    static_assert((BM * kBK64) % 1024 == 0, "A region must be whole 1 KB blocks");
+    static_assert(NS >= 3 && WM % 16 == 0 && WN % 16 == 0, "shape");
+
+    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStage];
+    __shared__ int s_tile_start[kMaxE + 1];
+    __shared__ int s_row_off[kMaxE];
+    __shared__ int s_rows[kMaxE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int N = p.N, Kred = p.Kred;
+    const int NB = (N + BN - 1) / BN;
+    const int total = build_tile_prefix<BM>(p, NB, s_tile_start, s_row_off, s_rows);
+
+    const int G = gridDim.x;  // a multiple of 8
+    const int vid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int wm0 = (wave / WAVES_N) * WM;
+    const int wn0 = (wave % WAVES_N) * WN;
+    const int nst = Kred / (kBK64 * S);              // stages; Kred is a multiple of 64 S
+    const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(&smem[0]));
+
+    // LDS byte offsets of this lane's fragment rows inside a 64-byte slice
+    int fa_off[TM], fb_off[TN];
+    {
+        const int chunk = lane >> 4;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn0 + 16 * j + (lane & 15);
-            if (col >= N) continue;
-            const float s = sc[col];
+        for (int i = 0; i < TM; ++i) fa_off[i] = lds_off64s(wm0 + 16 * i + (lane & 15), chunk);
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
+        for (int j = 0; j < TN; ++j)
+            fb_off[j] = BM * kBK64 + lds_off64s(wn0 + 16 * j + (lane & 15), chunk);
+    }
+
+    for (int t = vid; t < total; t += G) {
+        int lo = 0, hi = p.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_tile_start[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        const int e = lo;
+        const int rows_e = s_rows[e];
+        const int mb = (rows_e + BM - 1) / BM;
+        const int local = t - s_tile_start[e];
+        const int nblk = local / mb;
+        const int mblk = local - nblk * mb;
+        const int row0 = s_row_off[e] + mblk * BM;
+        const int rows = min(BM, rows_e - mblk * BM);
+        const int n0 = nblk * BN;
+
+        // DMA sources: block b of a stage is sub-step b / (kSub/1024), and
+        // inside it the lane fills LDS chunk pch of the slice.
+        const int8_t *src[LPW];
+        uint32_t dst[LPW];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int rl = wm0 + 16 * i + 4 * (lane >> 4) + v;
-                    if (rl < rows) {
-                        const size_t idx = (size_t)(row0 + rl) * N + col;
-                        const int a = acc[i][j][v];
-                        p.C[idx] = f2h(keep_f32((float)a * s));
-                        if (p.acc_dbg) p.acc_dbg[idx] = a;
-                    }
-                }
+        for (int j = 0; j < LPW; ++j) {
+            const int b = wave + j * NW;
+            const int ss = b / (kSub / 1024);
+            const int pch = (b % (kSub / 1024)) * 64 + lane;
+            dst[j] = (uint32_t)(b * 1024);
+            if (pch < BM * 4) {
+                const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
+                src[j] = p.A + (size_t)(row0 + min(r, rows - 1)) * Kred + ss * kBK64 + kc * 16;
+            } else {
+                const int q = pch - BM * 4;
+                const int r = q >> 2, kc = (q & 3) ^ swz64(q >> 2);
+                src[j] = p.B + ((size_t)e * N + min(n0 + r, N - 1)) * Kred + ss * kBK64 + kc * 16;
             }
         }
+        auto issue = [&](int stage) {
+            const int k0 = min(stage, nst - 1) * (kBK64 * S);
+            const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
+#pragma unroll
+            for (int j = 0; j < LPW; ++j)
+                dma16(src[j] + k0, __builtin_amdgcn_readfirstlane(sbase + dst[j]));
+        };
+        auto frag = [&](int stage, int ss, v4i *xa, v4i *xb) {
+            const int8_t *base = smem + (stage % NS) * kStage + ss * kSub;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) xa[i] = *reinterpret_cast<const v4i *>(base + fa_off[i]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const v4i *>(base + fb_off[j]);
+        };
+
+        v4i acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        v4i fa[2][TM], fb[2][TN];
+
+#pragma unroll
+        for (int st = 0; st < NS - 1; ++st) issue(st);
+        wait_vmcnt<(NS - 2) * LPW>();
+        __syncthreads();
+        frag(0, 0, fa[0], fb[0]);
+
+        // two stages per trip so that the register set of every sub-step is
+        // known at compile time (set = global sub-step index & 1)
+        for (int kt0 = 0; kt0 < nst; kt0 += 2) {
+            static_for<0, 2 * S>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;   // sub-step within the trip
+                constexpr int u = g / S, ss = g % S;
+                constexpr int cur = g & 1, nxt = cur ^ 1;
+                const int kt = kt0 + u;
+                if (kt < nst) {
+                    if constexpr (ss == S - 1) {
+                        wait_vmcnt<(NS - 3) * LPW>();
+                        __syncthreads();
+                        issue(kt + NS - 1);
+                        frag(kt + 1, 0, fa[nxt], fb[nxt]);
+                    } else {
+                        frag(kt, ss + 1, fa[nxt], fb[nxt]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = mfma_t(fb[cur][j], fa[cur][i], acc[i][j]);
+                }
+            });
+        }
+        // drain the prefetches past the end before the ring is reused
+        wait_vmcnt<0>();
+        __syncthreads();
+
+        store_tile<TM, TN>(p, acc, e, row0, rows, n0, wm0, wn0, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Direct pipeline: no LDS.  Each wave streams the fragments it multiplies
+// straight from global memory (L1/L2) into registers: lane l loads 16 bytes of
+// row (l & 15) at K chunk (l >> 4) of a 64-byte slice, which is exactly the
+// MFMA operand layout, for both the activation rows and the K-contiguous
+// weight rows.  Fragments shared by several waves are served by the caches.
+// A ring of D+1 register sets keeps D slices in flight; there are no barriers
+// and no LDS writes, the two costs that bound the LDS-staged pipelines.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WAVES_M, int WAVES_N, int D>
+__global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_direct_kernel(GmmParams p) {
+    constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    constexpr int TM = WM / 16, TN = WN / 16;
+    constexpr int NSET = D + 1;
+    static_assert(WM % 16 == 0 && WN % 16 == 0 && D >= 1, "shape");
+
+    __shared__ int s_tile_start[kMaxE + 1];
+    __shared__ int s_row_off[kMaxE];
+    __shared__ int s_rows[kMaxE];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int N = p.N, Kred = p.Kred;
+    const int NB = (N + BN - 1) / BN;
+    const int total = build_tile_prefix<BM>(p, NB, s_tile_start, s_row_off, s_rows);
+
+    const int G = gridDim.x;  // a multiple of 8
+    const int vid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int wm0 = (wave / WAVES_N) * WM;
+    const int wn0 = (wave % WAVES_N) * WN;
+    const int nk = Kred / kBK64;
+
+    for (int t = vid; t < total; t += G) {
+        int lo = 0, hi = p.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_tile_start[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        const int e = lo;
+        const int rows_e = s_rows[e];
+        const int mb = (rows_e + BM - 1) / BM;
+        const int local = t - s_tile_start[e];
+        const int nblk = local / mb;
+        const int mblk = local - nblk * mb;
+        const int row0 = s_row_off[e] + mblk * BM;
+        const int rows = min(BM, rows_e - mblk * BM);
+        const int n0 = nblk * BN;
+
+        const int8_t *pa[TM];
+        const int8_t *pb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = min(wm0 + 16 * i + (lane & 15), rows - 1);
+            pa[i] = p.A + (size_t)(row0 + r) * Kred + (lane >> 4) * 16;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = min(n0 + wn0 + 16 * j + (lane & 15), N - 1);
+            pb[j] = p.B + ((size_t)e * N + n) * Kred + (lane >> 4) * 16;
+        }
+
+        v4i fa[NSET][TM], fb[NSET][TN];
+        v4i acc[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+        auto load = [&](int stage, v4i *xa, v4i *xb) {
+            const int k0 = min(stage, nk - 1) * kBK64;  // past-the-end slices re-read the last
+#pragma unroll
+            for (int i = 0; i < TM; ++i) xa[i] = *reinterpret_cast<const v4i *>(pa[i] + k0);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) xb[j] = *reinterpret_cast<const v4i *>(pb[j] + k0);
+        };
+#pragma unroll
+        for (int u = 0; u < D; ++u) load(u, fa[u], fb[u]);
+
+        for (int kt0 = 0; kt0 < nk; kt0 += NSET) {
+            static_for<0, NSET>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;          // set holding slice kt
+                constexpr int ld = (u + D) % NSET;              // set for slice kt + D
+                const int kt = kt0 + u;
+                if (kt < nk) {
+                    load(kt + D, fa[ld], fb[ld]);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = mfma_t(fb[u][j], fa[u][i], acc[i][j]);
+                }
+            });
+        }
+
+        store_tile<TM, TN>(p, acc, e, row0, rows, n0, wm0, wn0, lane);
     }
 }
 
@@ -484,9 +732,9 @@ struct GmmVariant {
 };
 
 static GmmVariant g_variants[] = {
-    {64, 256, gmm_i8_pipe_kernel<64, 256, 1, 4, 3>, 256, 0},
-    {128, 256, gmm_i8_pipe_kernel<128, 256, 2, 4, 3>, 512, 0},
-    {256, 256, gmm_i8_dma_kernel<256, 256, 2, 4, 4>, 512, 0},
+    {64, 256, gmm_i8_ring_kernel<64, 256, 1, 4, 1, 6>, 256, 0},
+    {128, 256, gmm_i8_ring_kernel<128, 256, 2, 4, 1, 4>, 512, 0},
+    {256, 256, gmm_i8_ring_kernel<256, 256, 4, 4, 1, 4>, 1024, 0},
 };
 
 int gmm_num_variants() { return (int)(sizeof(g_variants) / sizeof(g_variants[0])); }
