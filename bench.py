@@ -42,6 +42,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens of the workload the oracle runs for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-profile", default=None, metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 kernel-trace directory into profiles/ and exit")
+    ap.add_argument("--pmc-fetch", default=None, help="rocprofv3 FETCH_SIZE output directory")
+    ap.add_argument("--pmc-write", default=None, help="rocprofv3 WRITE_SIZE output directory")
+    ap.add_argument("--command", default="", help="profiling command line recorded in the summary")
     return ap.parse_args()
 
 
@@ -107,8 +114,127 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (no GPU needed): kernel-trace stats and HBM traffic
+# ---------------------------------------------------------------------------
+STAGE_OF_KERNEL = {"route_count_kernel": "permute", "route_scatter_kernel": "permute",
+                   "quant_scatter_kernel": "permute", "swiglu_quant_kernel": "swiglu",
+                   "unpermute_kernel": "unpermute"}
+CALIB_BYTES = 1 << 30
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _label_dispatches(rows):
+    """Stage label per GEMM dispatch: the GEMM launch that follows the quant
+    scatter is GMM1, the one after SwiGLU is GMM2."""
+    out, last, seen_copy = [], None, set()
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        name = r["Kernel_Name"].split("(")[0].split("<")[0].replace("void ", "").strip()
+        name = name.split("::")[-1]
+        if name.startswith("gmm_i8"):
+            stage = "gmm1" if last == "quant_scatter_kernel" else "gmm2"
+        elif name in STAGE_OF_KERNEL:
+            stage = STAGE_OF_KERNEL[name]
+        elif "copyBuffer" in name and (not seen_copy or r["Dispatch_Id"] in seen_copy):
+            # the first device copy of the process is the 1 GiB calibration copy
+            seen_copy.add(r["Dispatch_Id"])
+            stage = "copy"
+        else:
+            stage = name
+        out.append((r, name, stage))
+        last = name
+    return out
+
+
+def summarize_profile(a):
+    from moe_expert_ffn_amd import inputs as W
+    w = W.WORKLOADS[a.workload]
+    trace = _csv_rows(_find(a.summarize_profile, "kernel_trace.csv"))
+    stats = _csv_rows(_find(a.summarize_profile, "kernel_stats.csv"))
+    per_stage = {}
+    for r, name, stage in _label_dispatches(trace):
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per_stage.setdefault(stage, []).append(dur)
+    steps = max(1, len(per_stage.get("gmm1", [])))
+    lines = [f"# rocprofv3 kernel trace: {w.describe()}", "",
+             "Command (from the repository root):", "", "```", a.command or "(not recorded)", "```",
+             "", "## rocprofv3 --stats (kernel_stats.csv)", "",
+             "| kernel | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    lines += ["", "## per pipeline stage and step (from the dispatch trace)", "",
+              "| stage | kernel launches per step | us per step |", "|---|---|---|"]
+    for st in STAGES:
+        v = per_stage.get(st, [])
+        if v:
+            lines.append(f"| {st} | {len(v) / steps:g} | {np.sum(v) / steps:.1f} |")
+    traffic = {}
+    if a.pmc_fetch and a.pmc_write:
+        def counter_avg(d, cname):
+            rows = _csv_rows(_find(d, "counter_collection.csv"))
+            acc = {}
+            for r, name, stage in _label_dispatches(rows):
+                if r["Counter_Name"] != cname:
+                    continue
+                acc.setdefault(stage, []).append(float(r["Counter_Value"]))
+            n = max(1, len(acc.get("gmm1", [])))  # pipeline steps in the run
+            return {k: float(np.sum(v)) / (1 if k == "copy" else n) for k, v in acc.items()}
+        fetch = counter_avg(a.pmc_fetch, "FETCH_SIZE")
+        write = counter_avg(a.pmc_write, "WRITE_SIZE")
+        # a plain copy of CALIB_BYTES reads and writes CALIB_BYTES: scale factors
+        f_scale = CALIB_BYTES / (fetch["copy"] * 1024.0)
+        w_scale = CALIB_BYTES / (write["copy"] * 1024.0)
+        lines += ["", "## HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
+                  f"Counter scale from a plain {CALIB_BYTES >> 20} MiB device copy: "
+                  f"FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f} "
+                  f"(raw copy: {fetch['copy']:.0f} KiB fetched, {write['copy']:.0f} KiB written).",
+                  "", "| stage (per step) | fetched MB | written MB | total MB |",
+                  "|---|---|---|---|"]
+        for st in STAGES:
+            if st not in fetch or st not in write:
+                continue
+            fb = fetch[st] * 1024 * f_scale
+            wb = write[st] * 1024 * w_scale
+            traffic[st] = fb + wb
+            lines.append(f"| {st} | {fb/1e6:.1f} | {wb/1e6:.1f} | {(fb+wb)/1e6:.1f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    md = os.path.join(ROOT, "profiles", f"pipeline_{w.name}.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    src = {"gmm1": "gmm.hip", "gmm2": "gmm.hip", "permute": "permute.hip",
+           "swiglu": "swiglu.hip", "unpermute": "unpermute.hip"}
+    for st, b in traffic.items():
+        if st not in src:
+            continue
+        rec = {"workload": w.name, "stage": st, "hbm_bytes_per_launch": round(b),
+               "source_sha256_16": source_hash(os.path.join(ROOT, "moe_expert_ffn_amd", "csrc",
+                                                            src[st])),
+               "command": a.command}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{st}_{w.name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    print(f"wrote {md}")
+
+
 def main():
     a = parse()
+    if a.summarize_profile:
+        summarize_profile(a)
+        return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {a.gpus} requested); the "
               "expert-parallel split across GPUs is not implemented here.", file=sys.stderr)
@@ -118,6 +244,13 @@ def main():
     from moe_expert_ffn_amd import megamoe as MM
 
     w = W.WORKLOADS[a.workload]
+    if a.copy_calibration:
+        src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inp = W.generate(w, a.seed)
     dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda") for k, v in inp.items()}
     d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
