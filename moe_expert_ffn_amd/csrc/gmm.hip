@@ -451,7 +451,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_dma_kernel(Gmm
 // last fragments were read before that barrier).  Stage kt+1 was issued NS-2
 // stages earlier, so at the barrier NS-3 stages may still be in flight.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WAVES_M, int WAVES_N, int S, int NS>
+// SKIP: waves whose rows all lie past the group's end skip their fragment
+// reads and MFMAs (costs registers; off for the 128-register configuration).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int S, int NS, bool SKIP = true>
 __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -510,6 +512,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         const int row0 = s_row_off[e] + mblk * BM;
         const int rows = min(BM, rows_e - mblk * BM);
         const int n0 = nblk * BN;
+        // a wave whose rows all lie past the group's end has nothing to multiply
+        const bool live = !SKIP || wm0 < rows;
 
         // DMA sources: block b of a stage is sub-step b / (kSub/1024), and
         // inside it the lane fills LDS chunk pch of the slice.
@@ -538,6 +542,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 dma16(src[j] + k0, __builtin_amdgcn_readfirstlane(sbase + dst[j]));
         };
         auto frag = [&](int stage, int ss, v4i *xa, v4i *xb) {
+            if (!live) return;
             const int8_t *base = smem + (stage % NS) * kStage + ss * kSub;
 #pragma unroll
             for (int i = 0; i < TM; ++i) xa[i] = *reinterpret_cast<const v4i *>(base + fa_off[i]);
@@ -575,11 +580,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                     } else {
                         frag(kt, ss + 1, fa[nxt], fb[nxt]);
                     }
+                    if (live) {
 #pragma unroll
-                    for (int i = 0; i < TM; ++i)
+                        for (int i = 0; i < TM; ++i)
 #pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            acc[i][j] = mfma_t(fb[cur][j], fa[cur][i], acc[i][j]);
+                            for (int j = 0; j < TN; ++j)
+                                acc[i][j] = mfma_t(fb[cur][j], fa[cur][i], acc[i][j]);
+                    }
                 }
             });
         }
@@ -734,7 +741,7 @@ struct GmmVariant {
 static GmmVariant g_variants[] = {
     {64, 256, gmm_i8_ring_kernel<64, 256, 1, 4, 1, 6>, 256, 0},
     {128, 256, gmm_i8_ring_kernel<128, 256, 2, 4, 1, 4>, 512, 0},
-    {256, 256, gmm_i8_ring_kernel<256, 256, 4, 4, 1, 4>, 1024, 0},
+    {256, 256, gmm_i8_ring_kernel<256, 256, 4, 4, 1, 4, false>, 1024, 0},
 };
 
 int gmm_num_variants() { return (int)(sizeof(g_variants) / sizeof(g_variants[0])); }
