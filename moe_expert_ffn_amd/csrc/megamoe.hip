@@ -84,7 +84,7 @@ int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const
             const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s) {
     const int R = d.M * d.top_k;
     GmmParams prm{A, Bp, scale, cumsum, C, dbg, d.E, N, Kred};
-    return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
+    return hip_status(launch_gmm(gmm_pick_variant(R, d.E, Kred), prm, R, cu_count_current(), s));
 }
 
 }  // namespace
