@@ -33,6 +33,8 @@ namespace megamoe {
 
 constexpr int kMaxE = 256;
 constexpr int kBK64 = 64;  // K bytes per MFMA step (one 64-byte slice per row)
+constexpr int kPackRows = 256;                 // weight rows per packed n-block (= BN)
+constexpr int kPackBlock = kPackRows * kBK64;  // bytes of one packed (n-block, K slice)
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
@@ -129,17 +131,21 @@ __device__ __forceinline__ void dma4(const void *gptr, uint32_t lds_base) {
 }
 
 // ---------------------------------------------------------------------------
-// Ring pipeline.  A stage is S sub-steps of 64 K-bytes ([S][BM + BN rows][64 B],
-// swizzled as above), copied by DMA into an NS-slot ring.  Fragments for the
-// next sub-step are read from LDS while the MFMAs of the current one run, so
-// the fragments of stage kt+1 are read during stage kt.  The barrier that
-// publishes stage kt+1 sits at the start of the last sub-step of stage kt; at
-// that point every wave has finished reading stage kt (its last fragments
-// went to registers during stage kt-1), so its slot is refilled with stage
-// kt+NS right after the barrier.  Stage kt+1 was issued NS-1 stages earlier
-// and NS-2 younger stages may still be in flight when it is awaited.  Copies
-// are issued for real stages only; over the last NS-2 stages of a tile, where
-// fewer younger copies exist, the wait is for all of them.
+// Ring pipeline.  A stage is one 64-byte K slice of the tile's BM A rows and
+// BN weight rows ([BM + BN rows][64 B], swizzled as above), copied by DMA
+// into an NS-slot ring.  Fragments for the next slice are read from LDS while
+// the MFMAs of the current one run, so the fragments of stage kt+1 are read
+// during stage kt.  The barrier that publishes stage kt+1 sits at the start of
+// stage kt; at that point every wave has finished reading stage kt (its
+// fragments went to registers during stage kt-1), so its slot is refilled with
+// stage kt+NS right after the barrier.  Stage kt+1 was issued NS-1 stages
+// earlier and NS-2 younger stages may still be in flight when it is awaited.
+// Copies are issued for real stages only; over the last NS-2 stages of a tile,
+// where fewer younger copies exist, the wait is for all of them.
+//
+// Weights are read from the tile-contiguous packed layout (see the pack
+// kernel): one stage of a tile's weight rows is a single contiguous 16 KB
+// block, so each tile streams its weights sequentially.
 //
 // The tile's per-channel scales are copied to one of two LDS slots (by tile
 // parity) when the tile starts, ahead of its stage copies in issue order, so
@@ -148,7 +154,7 @@ __device__ __forceinline__ void dma4(const void *gptr, uint32_t lds_base) {
 // SKIP: a wave whose rows all lie past the group's end (ragged last m-block of
 // an expert) runs a copy of the K loop without fragment reads and MFMAs; it
 // still issues its share of the copies and joins every barrier.  Each SIMD
-// hosts waves of every row block in the WAVES_M = 4 layouts, so a tile with r
+// hosts waves of every row block in the WAVES_M = 4 layout, so a tile with r
 // live row blocks costs about r / WAVES_M of a full one in MFMA time.
 // ---------------------------------------------------------------------------
 template <int TM, int TN>
@@ -178,19 +184,19 @@ __device__ __forceinline__ void store_tile_lds(const GmmParams &p, const v4i (&a
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int S, int NS, bool SKIP = true>
+template <int BM, int WAVES_M, int WAVES_N, int NS, bool SKIP = true>
 __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
+    constexpr int BN = kPackRows;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int kSub = (BM + BN) * kBK64;          // bytes of one 64-byte K slice
-    constexpr int kStage = kSub * S;
-    constexpr int kBlocks = kStage / 1024;
-    constexpr int LPW = kBlocks / NW;
-    static_assert(kSub % 1024 == 0 && kBlocks % NW == 0, "stage must split over the waves");
-    static_assert((BM * kBK64) % 1024 == 0, "A region must be whole 1 KB blocks");
+    constexpr int kStage = (BM + BN) * kBK64;        // bytes of one stage
+    constexpr int LPW = kStage / 1024 / NW;          // 1 KB copies per wave per stage
+    constexpr int kAJ = (BM / 16) / NW;              // copies j < kAJ fill A rows
+    static_assert(kStage % (1024 * NW) == 0, "stage must split over the waves");
+    static_assert((BM / 16) % NW == 0, "each wave fills the same number of A blocks");
     static_assert(NS >= 3 && WM % 16 == 0 && WN % 16 == 0, "shape");
-    static_assert(BN % kWave == 0 && BN / kWave <= NW, "one scale copy per wave at most");
+    static_assert(BN % kWave == 0, "scale copies are whole waves");
 
     __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStage];
     __shared__ __attribute__((aligned(16))) float s_scale[2][BN];
@@ -209,10 +215,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     const int vid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
     const int wm0 = (wave / WAVES_N) * WM;
     const int wn0 = (wave % WAVES_N) * WN;
-    const int nst = Kred / (kBK64 * S);              // stages; Kred is a multiple of 64 S
+    const int nst = Kred / kBK64;                    // stages (K slices)
     const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(&smem[0]));
 
-    // LDS byte offsets of this lane's fragment rows inside a 64-byte slice
+    // LDS byte offsets of this lane's fragment rows inside a stage
     int fa_off[TM], fb_off[TN];
     {
         const int chunk = lane >> 4;
@@ -242,36 +248,38 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         const int n0 = nblk * BN;
 
         // scales of the tile's columns (clamped: columns past N are never stored)
-        if (wave < BN / kWave)
-            dma4(p.scale + (size_t)e * N + min(n0 + wave * kWave + lane, N - 1),
-                 __builtin_amdgcn_readfirstlane(lds_addr(&s_scale[parity][wave * kWave])));
+        for (int c = wave; c < BN / kWave; c += NW)
+            dma4(p.scale + (size_t)e * N + min(n0 + c * kWave + lane, N - 1),
+                 __builtin_amdgcn_readfirstlane(lds_addr(&s_scale[parity][c * kWave])));
 
-        // DMA sources: block b of a stage is sub-step b / (kSub/1024), and
-        // inside it the lane fills LDS chunk pch of the slice.
+        // DMA sources: 1 KB block b = wave + j NW of a stage holds 16 rows;
+        // lane l fills LDS chunk l of the block (row 16 b + (l >> 2), slot
+        // l & 3), taking the chunk that the swizzle puts there.  A rows past
+        // the group's end repeat its last row (their results are not stored).
         const int8_t *src[LPW];
-        uint32_t dst[LPW];
+        const int8_t *btile =
+            p.B + ((size_t)e * NB + nblk) * (size_t)nst * kPackBlock;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int b = wave + j * NW;
-            const int ss = b / (kSub / 1024);
-            const int pch = (b % (kSub / 1024)) * 64 + lane;
-            dst[j] = (uint32_t)(b * 1024);
-            if (pch < BM * 4) {
+            const int pch = (wave + j * NW) * 64 + lane;
+            if (j < kAJ) {
                 const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
-                src[j] = p.A + (size_t)(row0 + min(r, rows - 1)) * Kred + ss * kBK64 + kc * 16;
+                src[j] = p.A + (size_t)(row0 + min(r, rows - 1)) * Kred + kc * 16;
             } else {
                 const int q = pch - BM * 4;
                 const int r = q >> 2, kc = (q & 3) ^ swz64(q >> 2);
-                src[j] = p.B + ((size_t)e * N + min(n0 + r, N - 1)) * Kred + ss * kBK64 + kc * 16;
+                src[j] = btile + r * kBK64 + kc * 16;
             }
         }
         auto issue = [&](int stage) {
             if (stage >= nst) return;
-            const int k0 = stage * (kBK64 * S);
             const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
 #pragma unroll
-            for (int j = 0; j < LPW; ++j)
-                dma16(src[j] + k0, __builtin_amdgcn_readfirstlane(sbase + dst[j]));
+            for (int j = 0; j < LPW; ++j) {
+                const size_t step = j < kAJ ? (size_t)kBK64 : (size_t)kPackBlock;
+                dma16(src[j] + (size_t)stage * step,
+                      __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024)));
+            }
         };
 
         v4i acc[TM][TN];
@@ -284,9 +292,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         auto kloop = [&](auto live_c) {
             constexpr bool LIVE = decltype(live_c)::value;
             v4i fa[2][TM], fb[2][TN];
-            auto frag = [&](int stage, int ss, v4i *xa, v4i *xb) {
+            auto frag = [&](int stage, v4i *xa, v4i *xb) {
                 if constexpr (LIVE) {
-                    const int8_t *base = smem + (stage % NS) * kStage + ss * kSub;
+                    const int8_t *base = smem + (stage % NS) * kStage;
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
                         xa[i] = *reinterpret_cast<const v4i *>(base + fa_off[i]);
@@ -300,35 +308,27 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             if (nst >= NS) wait_vmcnt<(NS - 1) * LPW>();
             else wait_vmcnt<0>();
             __syncthreads();
-            frag(0, 0, fa[0], fb[0]);
+            frag(0, fa[0], fb[0]);
 
-            // two stages per trip so that the register set of every sub-step
-            // is known at compile time (set = global sub-step index & 1)
+            // two stages per trip so that the register set of every stage is
+            // known at compile time (set = stage & 1); nst is even
             for (int kt0 = 0; kt0 < nst; kt0 += 2) {
-                static_for<0, 2 * S>([&](auto gc) {
-                    constexpr int g = decltype(gc)::value;   // sub-step within the trip
-                    constexpr int u = g / S, ss = g % S;
-                    constexpr int cur = g & 1, nxt = cur ^ 1;
-                    const int kt = kt0 + u;
-                    if (kt < nst) {
-                        if constexpr (ss == S - 1) {
-                            // stage kt+1 must have landed; stages up to kt+NS-1
-                            // were issued, the NS-2 after kt+1 may be in flight
-                            if (kt + NS - 1 < nst) wait_vmcnt<(NS - 2) * LPW>();
-                            else wait_vmcnt<0>();
-                            __syncthreads();
-                            issue(kt + NS);
-                            frag(kt + 1, 0, fa[nxt], fb[nxt]);
-                        } else {
-                            frag(kt, ss + 1, fa[nxt], fb[nxt]);
-                        }
-                        if constexpr (LIVE) {
+                static_for<0, 2>([&](auto uc) {
+                    constexpr int cur = decltype(uc)::value, nxt = cur ^ 1;
+                    const int kt = kt0 + cur;
+                    // stage kt+1 must have landed; stages up to kt+NS-1 were
+                    // issued, the NS-2 after kt+1 may be in flight
+                    if (kt + NS - 1 < nst) wait_vmcnt<(NS - 2) * LPW>();
+                    else wait_vmcnt<0>();
+                    __syncthreads();
+                    issue(kt + NS);
+                    frag(kt + 1, fa[nxt], fb[nxt]);
+                    if constexpr (LIVE) {
 #pragma unroll
-                            for (int i = 0; i < TM; ++i)
+                        for (int i = 0; i < TM; ++i)
 #pragma unroll
-                                for (int j = 0; j < TN; ++j)
-                                    acc[i][j] = mfma_t(fb[cur][j], fa[cur][i], acc[i][j]);
-                        }
+                            for (int j = 0; j < TN; ++j)
+                                acc[i][j] = mfma_t(fb[cur][j], fa[cur][i], acc[i][j]);
                     }
                 });
             }
@@ -342,44 +342,51 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     }
 }
 
-// Weight pack: logical [E][Kred][N] -> [E][N][Kred] (K-contiguous rows, so a
-// weight block of the GEMM is BN rows of 128 contiguous bytes per K slice).
-__global__ __launch_bounds__(256) void pack_kn_to_nk_kernel(const int8_t *__restrict__ w,
-                                                            int8_t *__restrict__ wp, int Kred,
-                                                            int N) {
+// Weight pack: logical [E][Kred][N] -> tile-contiguous [E][NB][Kred/64][256][64]
+// (NB = ceil(N / 256)): for n-block nb and K slice ks, the 256 weight rows
+// n = 256 nb + r hold bytes w[e][64 ks + kb][n], kb = 0..63, in one
+// contiguous 16 KB block; rows n >= N are zero.  One 64 x 64 (k, n) tile per
+// workgroup, transposed through LDS; its output is 64 rows of one block.
+__global__ __launch_bounds__(256) void pack_tiles_kernel(const int8_t *__restrict__ w,
+                                                         int8_t *__restrict__ wp, int Kred,
+                                                         int N, int NB) {
     __shared__ int8_t tile[64][65];
     const int e = blockIdx.z;
-    const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int ks = blockIdx.y, n0 = blockIdx.x * 64;
+    const int k0 = ks * kBK64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     const int8_t *src = w + (size_t)e * Kred * N;
-    int8_t *dst = wp + (size_t)e * N * Kred;
     for (int r = ty; r < 64; r += 4) {
         const int k = k0 + r, n = n0 + tx;
-        tile[r][tx] = (k < Kred && n < N) ? src[(size_t)k * N + n] : 0;
+        tile[r][tx] = n < N ? src[(size_t)k * N + n] : 0;
     }
     __syncthreads();
-    for (int r = ty; r < 64; r += 4) {
-        const int n = n0 + r, k = k0 + tx;
-        if (n < N && k < Kred) dst[(size_t)n * Kred + k] = tile[tx][r];
-    }
+    const int nb = n0 / kPackRows, r0 = n0 % kPackRows;
+    int8_t *dst = wp + (((size_t)e * NB + nb) * (Kred / kBK64) + ks) * kPackBlock;
+    for (int r = ty; r < 64; r += 4) dst[(size_t)(r0 + r) * kBK64 + tx] = tile[tx][r];
+}
+
+size_t packed_weight_bytes(int E, int Kred, int N) {
+    const size_t NB = (size_t)(N + kPackRows - 1) / kPackRows;
+    return (size_t)E * NB * kPackRows * (size_t)Kred;
 }
 
 hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipStream_t stream) {
-    dim3 grid((N + 63) / 64, (Kred + 63) / 64, E), block(256);
-    hipLaunchKernelGGL(pack_kn_to_nk_kernel, grid, block, 0, stream, w, wp, Kred, N);
+    const int NB = (N + kPackRows - 1) / kPackRows;
+    dim3 grid(NB * kPackRows / 64, Kred / kBK64, E), block(256);
+    hipLaunchKernelGGL(pack_tiles_kernel, grid, block, 0, stream, w, wp, Kred, N, NB);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Tile configurations, chosen by the host from the mean rows per expert and
-// the reduction length (measured on MI355X over the decode, mid, large and
-// skewed shapes):
+// Tile configurations, chosen by the host from the mean rows per expert
+// (measured on MI355X over the decode, mid, large and skewed shapes with
+// interleaved repetitions):
 //  * few rows per expert: the GEMM streams weights (HBM bound); a 64-row tile
-//    with wide weight blocks keeps every CU pulling weights;
-//  * many rows and a long reduction: 256 x 256 tiles on 8 waves (128 x 64
-//    per wave), the lower LDS read traffic per MFMA pays off;
-//  * many rows and a short reduction: 256 x 256 on 16 waves (64 x 64 per
-//    wave), finer dead-row skipping and shorter epilogues.
+//    with a 3-stage ring fits twice per CU, so two workgroups per CU keep
+//    twice the copies in flight;
+//  * more rows: MFMA bound; 256 x 256 tiles on 16 waves (64 x 64 per wave),
+//    which beat 8-wave layouts of the same tile on every shape measured.
 // ---------------------------------------------------------------------------
 struct GmmVariant {
     int bm, bn;
@@ -389,17 +396,15 @@ struct GmmVariant {
 };
 
 static GmmVariant g_variants[] = {
-    {64, 256, gmm_i8_ring_kernel<64, 256, 1, 4, 1, 4>, 256, 0},
-    {256, 256, gmm_i8_ring_kernel<256, 256, 2, 4, 1, 4>, 512, 0},
-    {256, 256, gmm_i8_ring_kernel<256, 256, 4, 4, 1, 4>, 1024, 0},
+    {64, 256, gmm_i8_ring_kernel<64, 1, 4, 3>, 256, 0},
+    {256, 256, gmm_i8_ring_kernel<256, 4, 4, 4>, 1024, 0},
 };
 
 int gmm_num_variants() { return (int)(sizeof(g_variants) / sizeof(g_variants[0])); }
 
-int gmm_pick_variant(int R, int E, int Kred) {
+int gmm_pick_variant(int R, int E) {
     const int mean = (R + E - 1) / E;
-    if (mean <= 96) return 0;
-    return Kred >= 4096 ? 1 : 2;
+    return mean <= 96 ? 0 : 1;
 }
 
 hipError_t launch_gmm(int variant, const GmmParams &prm, int R, int cu_count,

@@ -84,7 +84,7 @@ int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const
             const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s) {
     const int R = d.M * d.top_k;
     GmmParams prm{A, Bp, scale, cumsum, C, dbg, d.E, N, Kred};
-    return hip_status(launch_gmm(gmm_pick_variant(R, d.E, Kred), prm, R, cu_count_current(), s));
+    return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
 }
 
 }  // namespace
@@ -131,8 +131,8 @@ int megamoe_permute_workspace_bytes(const megamoe_dims *d, size_t *bytes) {
 int megamoe_packed_weight_bytes(const megamoe_dims *d, size_t *w1p, size_t *w2p) {
     MEGAMOE_TRY(megamoe_check_dims(d));
     if (!w1p || !w2p) return MEGAMOE_EINVAL;
-    *w1p = (size_t)d->E * d->K * 2 * d->I;
-    *w2p = (size_t)d->E * d->I * d->K;
+    *w1p = packed_weight_bytes(d->E, d->K, 2 * d->I);
+    *w2p = packed_weight_bytes(d->E, d->I, d->K);
     return MEGAMOE_OK;
 }
 

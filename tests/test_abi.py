@@ -56,6 +56,9 @@ def test_workspace_and_packed_sizes():
     assert ws >= R * 7168 + R * 4096 * 2 + R * 2048 + R * 7168 * 2
     assert ws < R * 7168 * 6
     assert MM.megamoe_packed_weight_bytes(d) == (32 * 7168 * 4096, 32 * 2048 * 7168)
+    # the packed layout pads each expert's output columns to whole 256-row blocks
+    d = MM.dims(64, 384, 16, 4, 128)
+    assert MM.megamoe_packed_weight_bytes(d) == (16 * 384 * 256, 16 * 128 * 512)
     assert MM.megamoe_permute_workspace_bytes(d) >= 4
     with pytest.raises(MM.MegaMoEError):
         MM.megamoe_workspace_bytes(MM.dims(4, 100, 4, 2, 128))

@@ -40,9 +40,9 @@ SMALL = [
     W.WORKLOADS["tiny"],
     W.custom(64, 384, 16, 4, 128, name="v0_mean16_raggedN"),        # 64-row tiles, N=384
     W.custom(200, 256, 6, 2, 256, name="v1_mean67"),                # 64-row tiles
-    W.custom(333, 512, 8, 3, 128, name="v2_mean125"),               # 256x256, 16 waves
-    W.custom(700, 256, 4, 2, 384, name="v3_mean350"),               # 256x256, 16 waves, ragged
-    W.custom(300, 4096, 5, 2, 256, name="v4_mean120_longK"),        # 256x256, 8 waves, dead waves (GMM1)
+    W.custom(333, 512, 8, 3, 128, name="v2_mean125"),               # 256x256 tiles
+    W.custom(700, 256, 4, 2, 384, name="v3_mean350"),               # 256x256 tiles, ragged
+    W.custom(300, 4096, 5, 2, 256, name="v4_mean120_longK"),        # 256x256, dead row blocks, long K
     W.custom(512, 256, 16, 4, 128, routing="zipf_empty", name="zipf_empty_groups"),
     W.custom(1, 128, 4, 2, 128, name="single_token"),
     W.custom(96, 640, 64, 6, 256, routing="zipf", name="skew_E64"),
