@@ -184,7 +184,7 @@ __device__ __forceinline__ void store_tile_lds(const GmmParams &p, const v4i (&a
     }
 }
 
-template <int BM, int WAVES_M, int WAVES_N, int NS, bool SKIP = true>
+template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true>
 __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
     constexpr int BN = kPackRows;
     constexpr int NW = WAVES_M * WAVES_N;
@@ -211,8 +211,19 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     const int NB = (N + BN - 1) / BN;
     const int total = build_tile_prefix<BM>(p, NB, s_tile_start, s_row_off, s_rows);
 
-    const int G = gridDim.x;  // a multiple of 8
-    const int vid = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    // TRIM (active grid, for tiles of equal cost that stream weights): with
+    // k = ceil(total / gridDim) tiles for the busiest workgroup, ceil(total / k)
+    // workgroups (rounded up to 8, the same number on every XCD) already finish
+    // in k rounds; the rest exit, so every active workgroup streams the same
+    // number of tiles and no last, partly filled round leaves HBM underused.
+    // Without TRIM all workgroups stay, which suits tiles of unequal cost.
+    const int per_xcd = gridDim.x >> 3;              // gridDim.x is a multiple of 8
+    const int rounds = (total + gridDim.x - 1) / gridDim.x;
+    const int act_xcd =
+        !TRIM ? per_xcd : rounds ? min(per_xcd, ((total + rounds - 1) / rounds + 7) >> 3) : 0;
+    if ((int)(blockIdx.x >> 3) >= act_xcd) return;
+    const int G = act_xcd << 3;
+    const int vid = (blockIdx.x & 7) * act_xcd + (blockIdx.x >> 3);
     const int wm0 = (wave / WAVES_N) * WM;
     const int wn0 = (wave % WAVES_N) * WN;
     const int nst = Kred / kBK64;                    // stages (K slices)
@@ -396,8 +407,8 @@ struct GmmVariant {
 };
 
 static GmmVariant g_variants[] = {
-    {64, 256, gmm_i8_ring_kernel<64, 1, 4, 3>, 256, 0},
-    {256, 256, gmm_i8_ring_kernel<256, 4, 4, 4>, 1024, 0},
+    {64, 256, gmm_i8_ring_kernel<64, 1, 4, 3, true>, 256, 0},
+    {256, 256, gmm_i8_ring_kernel<256, 4, 4, 4, false>, 1024, 0},
 };
 
 int gmm_num_variants() { return (int)(sizeof(g_variants) / sizeof(g_variants[0])); }

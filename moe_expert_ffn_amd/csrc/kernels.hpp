@@ -22,6 +22,13 @@ hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *s
                              int32_t *expanded_row_idx, int32_t *tokens_per_expert,
                              int32_t *expert_cumsum, int32_t *err_word, int32_t *block_counts,
                              hipStream_t stream);
+// Route sort and quant scatter in one launch, for R <= 8192 and top_k <= 16
+// (permute_fused_ok); same outputs as launch_route_sort + launch_quant_scatter.
+bool permute_fused_ok(int R, int top_k);
+hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, int M, int K, int E,
+                                int top_k, int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
+                                int32_t *sorted_route, int32_t *tokens_per_expert,
+                                int32_t *expert_cumsum, int32_t *err_word, hipStream_t stream);
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
                                 int top_k, int8_t *gmA, float *pts1, hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,

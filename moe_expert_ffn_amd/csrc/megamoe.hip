@@ -75,6 +75,9 @@ int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_
                 float *pts1, int32_t *eri, int32_t *sorted, int32_t *counts, int32_t *cumsum,
                 int32_t *err_word, int32_t *block_counts, hipStream_t s) {
     const int R = d.M * d.top_k;
+    if (permute_fused_ok(R, d.top_k))
+        return hip_status(launch_permute_fused(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA, pts1, eri,
+                                               sorted, counts, cumsum, err_word, s));
     MEGAMOE_TRY(hip_status(launch_route_sort(expert_idx, R, d.E, sorted, eri, counts, cumsum,
                                              err_word, block_counts, s)));
     return hip_status(launch_quant_scatter(x, eri, d.M, d.K, d.top_k, gmA, pts1, s));

@@ -233,6 +233,185 @@ __global__ __launch_bounds__(256) void quant_scatter_kernel(
     }
 }
 
+// Small route counts: the whole of FrontReorder in one launch, one workgroup
+// per token.  Every workgroup histograms all R expert ids in LDS (all routes,
+// and the routes before its own token), so it knows each expert's first row
+// and, for each of its own routes r, how many routes of the same expert come
+// before r -- the same stable expert-major order as the two-pass sort.  It
+// then quantises its token once and writes the row to its routes' rows.
+// Workgroup 0 also writes the counts, the inclusive prefix, the dropped-route
+// word and the -1 tail of sorted_route.  The x row is requested first, so its
+// load overlaps the histogram.
+constexpr int kFusedMaxR = 8192;
+constexpr int kFusedMaxTopK = 16;
+
+template <int MAXC>
+__global__ __launch_bounds__(256) void permute_fused_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ expert_idx, int R, int E,
+    int K, int top_k, int8_t *__restrict__ gmA, float *__restrict__ pts1,
+    int32_t *__restrict__ expanded_row_idx, int32_t *__restrict__ sorted_route,
+    int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_cumsum,
+    int32_t *__restrict__ err_word) {
+    __shared__ int h_all[kMaxExperts + 1];
+    __shared__ int h_pre[kMaxExperts + 1];
+    __shared__ int s_key[kFusedMaxTopK];
+    __shared__ int s_dst[kFusedMaxTopK];
+    __shared__ float s_red[4];
+    __shared__ int s_valid;
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int nchunk = K >> 4;
+    const int r_own = t * top_k;
+
+    // the token's row, requested before anything else
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)t * K);
+    uint4 raw[MAXC][2];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c < nchunk) {
+            raw[i][0] = xr[2 * c];
+            raw[i][1] = xr[2 * c + 1];
+        }
+    }
+
+    for (int e = tid; e <= E; e += 256) {
+        h_all[e] = 0;
+        h_pre[e] = 0;
+    }
+    if (tid < top_k) s_key[tid] = route_key(expert_idx, r_own + tid, R, E);
+    __syncthreads();
+    for (int r0 = 0; r0 < R; r0 += 8 * 256) {
+        int key[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) key[u] = route_key(expert_idx, r0 + u * 256 + tid, R, E);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = r0 + u * 256 + tid;
+            if (r < R) {  // key E (dropped) is counted too, in slot E
+                atomicAdd(&h_all[key[u]], 1);
+                if (r < r_own) atomicAdd(&h_pre[key[u]], 1);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {  // exclusive prefix of the counts over experts, four per lane
+        int v[4];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane * 4 + j;
+            v[j] = (e < E) ? h_all[e] : 0;
+            sum += v[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        int run = incl - sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane * 4 + j;
+            if (e < E) {
+                if (t == 0) {
+                    tokens_per_expert[e] = v[j];
+                    expert_cumsum[e] = run + v[j];
+                }
+                h_pre[e] += run;  // first row of expert e for this token's routes
+            }
+            run += v[j];
+        }
+        if (lane == kWave - 1) s_valid = incl;
+    }
+    __syncthreads();
+    if (tid < top_k) {
+        const int key = s_key[tid];
+        int dst = -1;
+        if (key < E) {
+            int same = 0;  // earlier slots of this token with the same expert
+            for (int u = 0; u < tid; ++u) same += s_key[u] == key;
+            dst = h_pre[key] + same;
+        }
+        s_dst[tid] = dst;
+        expanded_row_idx[r_own + tid] = dst;
+        if (dst >= 0) sorted_route[dst] = r_own + tid;
+    }
+    if (t == 0) {
+        const int valid_rows = s_valid;
+        if (tid == 0) err_word[0] = R - valid_rows;
+        for (int d = valid_rows + tid; d < R; d += 256) sorted_route[d] = -1;
+    }
+
+    // per-token dynamic quantisation, written to every route's row
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c < nchunk) {
+            const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] & 0xffffu))));
+                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] >> 16))));
+            }
+        }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) s_red[tid >> 6] = amax;
+    __syncthreads();  // also publishes s_dst
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float scale = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c >= nchunk) continue;
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
+        uint32_t packed[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int idx = j * 4 + h;
+                const uint16_t bits = (uint16_t)((w[idx >> 1] >> ((idx & 1) * 16)) & 0xffffu);
+                int q = 0;
+                if (amax != 0.0f) {
+                    float r = roundf(h2f(bits) / scale);  // CAST_ROUND: half away from zero
+                    r = fminf(fmaxf(r, -127.0f), 127.0f);
+                    q = (int)r;
+                }
+                word |= ((uint32_t)q & 0xffu) << (8 * h);
+            }
+            packed[j] = word;
+        }
+        const uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        for (int s2 = 0; s2 < top_k; ++s2) {
+            const int d = s_dst[s2];
+            if (d >= 0) *reinterpret_cast<uint4 *>(gmA + (size_t)d * K + (size_t)c * 16) = out;
+        }
+    }
+    if (tid < top_k && s_dst[tid] >= 0) pts1[s_dst[tid]] = scale;
+}
+
+bool permute_fused_ok(int R, int top_k) { return R <= kFusedMaxR && top_k <= kFusedMaxTopK; }
+
+hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, int M, int K, int E,
+                                int top_k, int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
+                                int32_t *sorted_route, int32_t *tokens_per_expert,
+                                int32_t *expert_cumsum, int32_t *err_word, hipStream_t stream) {
+    const int R = M * top_k;
+    const int per_thread = (K / 16 + 255) / 256;
+    dim3 grid(M), block(256);
+#define MEGAMOE_PERMUTE_FUSED(C)                                                              \
+    hipLaunchKernelGGL(permute_fused_kernel<C>, grid, block, 0, stream, x, expert_idx, R, E, K, \
+                       top_k, gmA, pts1, expanded_row_idx, sorted_route, tokens_per_expert,     \
+                       expert_cumsum, err_word)
+    if (per_thread <= 1) MEGAMOE_PERMUTE_FUSED(1);
+    else if (per_thread <= 2) MEGAMOE_PERMUTE_FUSED(2);
+    else if (per_thread <= 4) MEGAMOE_PERMUTE_FUSED(4);
+    else MEGAMOE_PERMUTE_FUSED(8);
+#undef MEGAMOE_PERMUTE_FUSED
+    return hipGetLastError();
+}
+
 // Routes per sort block: at least 256, and at most 256 blocks so that each
 // block's pass over the block-count table stays short.
 int route_sort_chunk(int R) {

@@ -19,12 +19,24 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
     const int32_t *__restrict__ expert_cumsum, int E, int I, int8_t *__restrict__ q2,
     float *__restrict__ pts2) {
     __shared__ float s_red[4];
-    const int row = blockIdx.x;
-    if (row >= expert_cumsum[E - 1]) return;  // only valid rows carry data
+    const int row = blockIdx.x;  // < R: gmC and pts1 hold R rows
     const int tid = threadIdx.x;
     const int nchunk = I >> 3;
-    const float p1 = pts1[row];
     const uint16_t *crow = gmC + (size_t)row * (2 * I);
+
+    // the row's loads go out before the validity check so that both memory
+    // round trips overlap; rows past the valid count are read, never written
+    uint4 uraw[MAXC], graw[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c < nchunk) {
+            uraw[i] = *reinterpret_cast<const uint4 *>(crow + c * 8);
+            graw[i] = *reinterpret_cast<const uint4 *>(crow + I + c * 8);
+        }
+    }
+    const float p1 = pts1[row];
+    if (row >= expert_cumsum[E - 1]) return;  // only valid rows carry data
 
     float y[MAXC][8];
     float amax = 0.0f;
@@ -32,10 +44,8 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
     for (int i = 0; i < MAXC; ++i) {
         const int c = tid + i * 256;
         if (c < nchunk) {
-            const uint4 uraw = *reinterpret_cast<const uint4 *>(crow + c * 8);
-            const uint4 graw = *reinterpret_cast<const uint4 *>(crow + I + c * 8);
-            const uint32_t *uw = reinterpret_cast<const uint32_t *>(&uraw);
-            const uint32_t *gw = reinterpret_cast<const uint32_t *>(&graw);
+            const uint32_t *uw = reinterpret_cast<const uint32_t *>(&uraw[i]);
+            const uint32_t *gw = reinterpret_cast<const uint32_t *>(&graw[i]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float u = h2f((uint16_t)((uw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;

@@ -9,11 +9,16 @@
 //
 // The page found fp32 atomics slower than a gather for this step; this kernel
 // is a pure gather: each thread owns 8 output columns of one token and reads
-// the matching 16 bytes of every slot's row.
+// the matching 16 bytes of every slot's row.  Slots are handled in batches of
+// 8: the batch's row indices, scales and row chunks are all requested before
+// any is used, so a token costs two memory round trips per batch instead of
+// two per slot; the sum still runs over the slots in order.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace megamoe {
+
+constexpr int kSlotBatch = 8;
 
 __global__ __launch_bounds__(256) void unpermute_kernel(
     const uint16_t *__restrict__ gmm2_out, const float *__restrict__ pts2,
@@ -29,19 +34,34 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
 
-    for (int s = 0; s < top_k; ++s) {
-        const int d = rows[s];
-        if (d < 0) continue;  // dropped route
-        const float sc = pts2[d];
-        const float p = pr[s];
-        const uint4 raw = *reinterpret_cast<const uint4 *>(gmm2_out + (size_t)d * K + c * 8);
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw);
+    for (int s0 = 0; s0 < top_k; s0 += kSlotBatch) {
+        int d[kSlotBatch];
+        float p[kSlotBatch], sc[kSlotBatch];
+        uint4 raw[kSlotBatch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float g = h2f((uint16_t)((w[j >> 1] >> ((j & 1) * 16)) & 0xffffu));
-            const float deq = bf2f(f2bf(g * sc));  // combine: cast to the output type
-            const float weighted = deq * p;
-            acc[j] = acc[j] + weighted;
+        for (int u = 0; u < kSlotBatch; ++u) {
+            const bool in = s0 + u < top_k;
+            d[u] = in ? rows[s0 + u] : -1;
+            p[u] = in ? pr[s0 + u] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+            if (d[u] >= 0) {  // d < 0: dropped route or past top_k
+                sc[u] = pts2[d[u]];
+                raw[u] = *reinterpret_cast<const uint4 *>(gmm2_out + (size_t)d[u] * K + c * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSlotBatch; ++u) {
+            if (d[u] < 0) continue;
+            const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[u]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float g = h2f((uint16_t)((w[j >> 1] >> ((j & 1) * 16)) & 0xffffu));
+                const float deq = bf2f(f2bf(g * sc[u]));  // combine: cast to the output type
+                const float weighted = deq * p[u];
+                acc[j] = acc[j] + weighted;
+            }
         }
     }
     uint32_t o[4];
