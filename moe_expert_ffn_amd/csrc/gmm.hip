@@ -254,8 +254,17 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         const int local = t - s_tile_start[e];
         const int nblk = local / mb;
         const int mblk = local - nblk * mb;
-        const int row0 = s_row_off[e] + mblk * BM;
-        const int rows = min(BM, rows_e - mblk * BM);
+        // the group's rows, in units of one wave row block, are split as evenly
+        // as the mb m-blocks allow (530 rows: 192 + 192 + 146, not 256 + 256 +
+        // 18): a ragged last block would stream a full tile's weights for a
+        // quarter of the MFMA work
+        constexpr int kUnit = BM / WAVES_M;
+        const int nu = (rows_e + kUnit - 1) / kUnit;
+        const int uq = nu / mb, ur = nu - uq * mb;
+        const int first = kUnit * (mblk * uq + min(mblk, ur));
+        const int last = min(rows_e, kUnit * ((mblk + 1) * uq + min(mblk + 1, ur)));
+        const int row0 = s_row_off[e] + first;
+        const int rows = last - first;
         const int n0 = nblk * BN;
 
         // scales of the tile's columns (clamped: columns past N are never stored)
