@@ -43,6 +43,7 @@ SMALL = [
     W.custom(333, 512, 8, 3, 128, name="v2_mean125"),               # 256x256 tiles
     W.custom(700, 256, 4, 2, 384, name="v3_mean350"),               # 256x256 tiles, ragged
     W.custom(300, 4096, 5, 2, 256, name="v4_mean120_longK"),        # 256x256, dead row blocks, long K
+    W.custom(256, 512, 64, 8, 2048, name="v5_two_tiles_per_wg"),    # 64-row tiles, 2 per workgroup
     W.custom(512, 256, 16, 4, 128, routing="zipf_empty", name="zipf_empty_groups"),
     W.custom(1, 128, 4, 2, 128, name="single_token"),
     W.custom(96, 640, 64, 6, 256, routing="zipf", name="skew_E64"),
@@ -91,6 +92,11 @@ def test_stages_and_forward_small(w):
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == o_ref["dropped"]
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
+    # the GEMMs without debug accumulators (the path the forward takes) store
+    # the same fp16 tiles
+    g_fast = H.run_stages(w, dev, w1p, w2p, debug_acc=False)
+    for k in ("gmC", "gmm2_out"):
+        assert torch.equal(g_fast[k].view(torch.int16), g[k].view(torch.int16)), k
 
 
 def test_hot_expert_and_duplicates():
@@ -172,6 +178,12 @@ def test_full_size_sampled(name):
     assert dropped == 0 and g["dropped"] == 0
     # the forward (timed by the benchmark) equals the staged run
     assert np.array_equal(H.bf16_bits(out_fwd), H.bf16_bits(g["out"]))
+    # GEMM tiles without debug accumulators (the forward's path) are the same
+    # fp16 values as with them
+    g_fast = H.run_stages(w, dev, w1p, w2p, debug_acc=False)
+    for k in ("gmC", "gmm2_out"):
+        assert torch.equal(g_fast[k].view(torch.int16), g[k].view(torch.int16)), k
+    del g_fast
 
     # sort metadata: bit-exact everywhere
     srt = O.route_sort(inp["expert_idx"], w.E)
