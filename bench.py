@@ -6,8 +6,10 @@ SwiGLU + re-quant, GMM2, combine + unpermute) over one batch of synthetic
 inputs already resident in HBM.  The default workload is the decode-size
 forward (M=128, K=7168, E=32, top-k 8, I=2048).  Prints ONE JSON line.
 
-Timing.  The headline step is one megamoe_forward call: W untimed steps, then
-K timed steps enqueued back to back between two device synchronisations.  The
+Timing.  The headline step is one megamoe_forward call: about 0.2 s of
+untimed calls (the clocks of an idle GPU take that long to settle under load),
+W untimed steps, then K timed steps enqueued back to back between two device
+synchronisations.  The
 per-stage durations (and the roofline of the dominant kernel) come from a
 second timed loop of K steps that calls the per-stage entry points of the C
 ABI -- the same kernels, in the same order, as megamoe_forward -- with HIP
@@ -313,7 +315,16 @@ def main():
         MM.megamoe_forward(d, dev["x"], dev["expert_idx"], dev["probs"], w1p, dev["scale1"], w2p,
                            dev["scale2"], out, fws)
 
-    # headline: K forward calls, back to back
+    # headline: K forward calls, back to back.  The clocks of an idle GPU take
+    # a while to settle under load, so about 0.2 s of untimed forward calls
+    # precede the W counted warm-up steps.
+    t_pre = time.perf_counter()
+    while True:
+        for _ in range(4):
+            fwd()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_pre > 0.2:
+            break
     for _ in range(a.warmup):
         fwd()
     torch.cuda.synchronize()

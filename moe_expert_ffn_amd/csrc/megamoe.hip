@@ -18,6 +18,11 @@ constexpr size_t kErrBytes = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// The four large intermediates start on 2 MiB boundaries, as separate device
+// allocations of their size would.
+constexpr size_t kBigAlign = 2u << 20;
+size_t align_big(size_t v) { return (v + kBigAlign - 1) / kBigAlign * kBigAlign; }
+
 bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 int cu_count_current() {
@@ -55,9 +60,10 @@ Layout forward_layout(const megamoe_dims &d) {
     L.cumsum = o; o += align_up((size_t)d.E * 4);
     L.pts1 = o;   o += align_up(R * 4);
     L.pts2 = o;   o += align_up(R * 4);
-    L.gmA = o;    o += align_up(R * d.K);
-    L.gmC = o;    o += align_up(R * 2 * d.I * 2);
-    L.q2 = o;     o += align_up(R * d.I);
+    o = align_big(o);
+    L.gmA = o;    o = align_big(o + R * d.K);
+    L.gmC = o;    o = align_big(o + R * 2 * d.I * 2);
+    L.q2 = o;     o = align_big(o + R * d.I);
     L.g2 = o;     o += align_up(R * d.K * 2);
     L.total = o;
     return L;

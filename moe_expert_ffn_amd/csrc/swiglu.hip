@@ -6,30 +6,32 @@
 // half, then quantise the row again: scale2 = max|y| / 127 and
 // q = CAST_RINT(y * (127 / max|y|)).
 //
-// One workgroup per row; each thread keeps its 8-column chunks of y in
-// registers so the row maximum needs a single pass over HBM.
+// One wave per row, four rows per workgroup: each lane keeps its 8-column
+// chunks of y in registers, so the row maximum is a wave reduction and the
+// row needs a single pass over HBM.  Every load of the row is issued before
+// the validity check, so the two memory round trips overlap.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace megamoe {
 
+constexpr int kRowsPerBlock = 4;
+
 template <int MAXC>
-__global__ __launch_bounds__(256) void swiglu_quant_kernel(
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void swiglu_quant_kernel(
     const uint16_t *__restrict__ gmC, const float *__restrict__ pts1,
-    const int32_t *__restrict__ expert_cumsum, int E, int I, int8_t *__restrict__ q2,
+    const int32_t *__restrict__ expert_cumsum, int R, int E, int I, int8_t *__restrict__ q2,
     float *__restrict__ pts2) {
-    __shared__ float s_red[4];
-    const int row = blockIdx.x;  // < R: gmC and pts1 hold R rows
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= R) return;  // wave-uniform; gmC and pts1 hold R rows
     const int nchunk = I >> 3;
     const uint16_t *crow = gmC + (size_t)row * (2 * I);
 
-    // the row's loads go out before the validity check so that both memory
-    // round trips overlap; rows past the valid count are read, never written
     uint4 uraw[MAXC], graw[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
+        const int c = lane + i * kWave;
         if (c < nchunk) {
             uraw[i] = *reinterpret_cast<const uint4 *>(crow + c * 8);
             graw[i] = *reinterpret_cast<const uint4 *>(crow + I + c * 8);
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
+        const int c = lane + i * kWave;
         if (c < nchunk) {
             const uint32_t *uw = reinterpret_cast<const uint32_t *>(&uraw[i]);
             const uint32_t *gw = reinterpret_cast<const uint32_t *>(&graw[i]);
@@ -52,24 +54,21 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
                 const float g = h2f((uint16_t)((gw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;
                 const float ex = expf(u * -1.0f);
                 const float den = ex + 1.0f;
-                const float s = u / den;
-                const float v = s * g;
+                const float sl = u / den;
+                const float v = sl * g;
                 y[i][j] = v;
                 amax = fmaxf(amax, fabsf(v));
             }
         }
     }
     amax = wave_max(amax);
-    if ((tid & 63) == 0) s_red[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     const float scale2 = amax / 127.0f;
     const float mul = 127.0f / amax;
 
     int8_t *qrow = q2 + (size_t)row * I;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
+        const int c = lane + i * kWave;
         if (c >= nchunk) continue;
         uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -85,26 +84,25 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(
         }
         *reinterpret_cast<uint2 *>(qrow + c * 8) = make_uint2(lo, hi);
     }
-    if (tid == 0) pts2[row] = scale2;
+    if (lane == 0) pts2[row] = scale2;
 }
 
 hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,
                                const int32_t *expert_cumsum, int R, int E, int I, int8_t *q2,
                                float *pts2, hipStream_t stream) {
-    const int per_thread = (I / 8 + 255) / 256;
-    dim3 grid(R), block(256);
-    if (per_thread <= 1)
-        hipLaunchKernelGGL(swiglu_quant_kernel<1>, grid, block, 0, stream, gmC, pts1,
-                           expert_cumsum, E, I, q2, pts2);
-    else if (per_thread <= 2)
-        hipLaunchKernelGGL(swiglu_quant_kernel<2>, grid, block, 0, stream, gmC, pts1,
-                           expert_cumsum, E, I, q2, pts2);
-    else if (per_thread <= 4)
-        hipLaunchKernelGGL(swiglu_quant_kernel<4>, grid, block, 0, stream, gmC, pts1,
-                           expert_cumsum, E, I, q2, pts2);
-    else
-        hipLaunchKernelGGL(swiglu_quant_kernel<8>, grid, block, 0, stream, gmC, pts1,
-                           expert_cumsum, E, I, q2, pts2);
+    const int per_lane = (I / 8 + kWave - 1) / kWave;  // I <= 16384: at most 32
+    dim3 grid((R + kRowsPerBlock - 1) / kRowsPerBlock), block(kRowsPerBlock * kWave);
+#define MEGAMOE_SWIGLU(C)                                                                 \
+    hipLaunchKernelGGL(swiglu_quant_kernel<C>, grid, block, 0, stream, gmC, pts1, expert_cumsum, \
+                       R, E, I, q2, pts2)
+    if (per_lane <= 1) MEGAMOE_SWIGLU(1);
+    else if (per_lane <= 2) MEGAMOE_SWIGLU(2);
+    else if (per_lane <= 3) MEGAMOE_SWIGLU(3);
+    else if (per_lane <= 4) MEGAMOE_SWIGLU(4);
+    else if (per_lane <= 8) MEGAMOE_SWIGLU(8);
+    else if (per_lane <= 16) MEGAMOE_SWIGLU(16);
+    else MEGAMOE_SWIGLU(32);
+#undef MEGAMOE_SWIGLU
     return hipGetLastError();
 }
 
