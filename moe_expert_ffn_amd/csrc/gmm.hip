@@ -32,6 +32,7 @@
 namespace megamoe {
 
 constexpr int kMaxE = 256;
+constexpr int kMaxWorkgroups = 1024;  // GEMM grid bound (cost table of the last round)
 constexpr int kBK64 = 64;  // K bytes per MFMA step (one 64-byte slice per row)
 constexpr int kPackRows = 256;                 // weight rows per packed n-block (= BN)
 constexpr int kPackBlock = kPackRows * kBK64;  // bytes of one packed (n-block, K slice)
@@ -72,6 +73,35 @@ __device__ __forceinline__ int build_tile_prefix(const GmmParams &p, int NB, int
     }
     __syncthreads();
     return s_tile_start[p.E];
+}
+
+// Rows of tile t, from the LDS tile prefix: expert e's rows are split over its
+// m-blocks as evenly as whole units (one wave row block each) allow -- 530 rows
+// become 192 + 192 + 146, not 256 + 256 + 18, since a ragged last block would
+// stream a full tile's weights for a fraction of the MFMA work.  Tiles of one
+// expert are ordered n-block-major, m-blocks innermost.
+struct TileRows {
+    int e, row0, rows, nblk;
+};
+template <int BM, int UNIT>
+__device__ __forceinline__ TileRows tile_rows(int t, int E, const int *s_tile_start,
+                                              const int *s_row_off, const int *s_rows) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tile_start[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int rows_e = s_rows[lo];
+    const int mb = (rows_e + BM - 1) / BM;
+    const int local = t - s_tile_start[lo];
+    const int nblk = local / mb;
+    const int mblk = local - nblk * mb;
+    const int nu = (rows_e + UNIT - 1) / UNIT;
+    const int uq = nu / mb, ur = nu - uq * mb;
+    const int first = UNIT * (mblk * uq + min(mblk, ur));
+    const int last = min(rows_e, UNIT * ((mblk + 1) * uq + min(mblk + 1, ur)));
+    return TileRows{lo, s_row_off[lo] + first, last - first, nblk};
 }
 
 // The MFMAs compute the transposed tile (weight fragment as the first operand,
@@ -240,32 +270,48 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             fb_off[j] = BM * kBK64 + lds_off64s(wn0 + 16 * j + (lane & 15), chunk);
     }
 
-    int parity = 0;
-    for (int t = vid; t < total; t += G, parity ^= 1) {
-        int lo = 0, hi = p.E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_tile_start[mid] <= t) lo = mid;
-            else hi = mid - 1;
+    // Tiles vid, vid + G, ... for the F full rounds.  When the last round is
+    // sparse (L <= G / 4 tiles), its tiles go to the workgroups whose full
+    // rounds cost least (live row blocks summed over their tiles; ties by
+    // position): every workgroup computes all G costs and its own rank the same
+    // way.  Tiles of unequal cost (ragged groups) otherwise leave the few
+    // workgroups of that round finishing long after the rest.  A fuller last
+    // round keeps the plain order, whose adjacent tiles share L2 data.
+    __shared__ int s_cost[kMaxWorkgroups];
+    __shared__ int s_extra;
+    const int F = total / G, L = total - F * G;
+    const bool ranked = !TRIM && L > 0 && 4 * L <= G;
+    if (ranked) {
+        for (int w = tid; w < G; w += NW * kWave) {
+            int c = 0;
+            for (int k = 0; k < F; ++k) {
+                const TileRows tr =
+                    tile_rows<BM, BM / WAVES_M>(w + k * G, p.E, s_tile_start, s_row_off, s_rows);
+                c += (tr.rows + WM - 1) / WM;
+            }
+            s_cost[w] = c;
         }
-        const int e = lo;
-        const int rows_e = s_rows[e];
-        const int mb = (rows_e + BM - 1) / BM;
-        const int local = t - s_tile_start[e];
-        const int nblk = local / mb;
-        const int mblk = local - nblk * mb;
-        // the group's rows, in units of one wave row block, are split as evenly
-        // as the mb m-blocks allow (530 rows: 192 + 192 + 146, not 256 + 256 +
-        // 18): a ragged last block would stream a full tile's weights for a
-        // quarter of the MFMA work
-        constexpr int kUnit = BM / WAVES_M;
-        const int nu = (rows_e + kUnit - 1) / kUnit;
-        const int uq = nu / mb, ur = nu - uq * mb;
-        const int first = kUnit * (mblk * uq + min(mblk, ur));
-        const int last = min(rows_e, kUnit * ((mblk + 1) * uq + min(mblk + 1, ur)));
-        const int row0 = s_row_off[e] + first;
-        const int rows = last - first;
-        const int n0 = nblk * BN;
+        __syncthreads();
+        if (tid == 0) {
+            const int mine = s_cost[vid];
+            int rank = 0;
+            for (int w = 0; w < G; ++w) rank += s_cost[w] < mine || (s_cost[w] == mine && w < vid);
+            s_extra = rank < L ? F * G + rank : -1;
+        }
+        __syncthreads();
+    }
+    const int extra = ranked ? s_extra : (vid < L ? F * G + vid : -1);
+
+    int parity = 0;
+    for (int k = 0;; ++k, parity ^= 1) {
+        const int t = k < F ? vid + k * G : (k == F ? extra : -1);
+        if (t < 0) break;
+        const TileRows tr = tile_rows<BM, BM / WAVES_M>(t, p.E, s_tile_start, s_row_off, s_rows);
+        const int e = tr.e;
+        const int row0 = tr.row0;
+        const int rows = tr.rows;
+        const int n0 = tr.nblk * BN;
+        const int nblk = tr.nblk;
 
         // scales of the tile's columns (clamped: columns past N are never stored)
         for (int c = wave; c < BN / kWave; c += NW)
@@ -444,6 +490,7 @@ hipError_t launch_gmm(int variant, const GmmParams &prm, int R, int cu_count,
     if (ub < g) g = ub;
     g = (g + 7) / 8 * 8;
     if (g < 8) g = 8;
+    if (g > kMaxWorkgroups) g = kMaxWorkgroups;
     hipLaunchKernelGGL(v.kernel, dim3((unsigned)g), dim3(v.threads), 0, stream, prm);
     return hipGetLastError();
 }
