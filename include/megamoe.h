@@ -85,7 +85,11 @@ int megamoe_prepack_w2(const megamoe_dims *d, const int8_t *w2, int8_t *w2p, voi
  *   scale2     fp32  [E, K]       GMM2 per-output-channel dequant scale
  *   out        bf16  [M, K]
  *   workspace  >= megamoe_workspace_bytes(); the caller may not touch it while
- *              the forward runs.  Intermediates live there. */
+ *              the forward runs.  Intermediates live there.
+ * The result equals, bit for bit, that of the five stage entry points below
+ * run in order.  Internally the forward keeps the quantised tokens token-major
+ * ([M, K], each written once) and GMM1 gathers its expert-sorted rows from
+ * them through the route list, instead of materialising the [R, K] gmA. */
 int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
                     const float *probs, const int8_t *w1p, const float *scale1,
                     const int8_t *w2p, const float *scale2, uint16_t *out,

@@ -330,7 +330,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             const int pch = (wave + j * NW) * 64 + lane;
             if (j < kAJ) {
                 const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
-                src[j] = p.A + (size_t)(row0 + min(r, rows - 1)) * Kred + kc * 16;
+                const int arow = row0 + min(r, rows - 1);
+                const int srow = p.a_route ? p.a_route[arow] / p.a_div : arow;
+                src[j] = p.A + (size_t)srow * Kred + kc * 16;
             } else {
                 const int q = pch - BM * 4;
                 const int r = q >> 2, kc = (q & 3) ^ swz64(q >> 2);

@@ -14,6 +14,10 @@ struct GmmParams {
     uint16_t *C;              // [rows, N] fp16
     int32_t *acc_dbg;         // nullable [rows, N] int32 accumulators
     int E, N, Kred;
+    // nullable: A row d is read from row a_route[d] / a_div of A (a token-major
+    // A gathered through the sorted route list)
+    const int32_t *a_route = nullptr;
+    int a_div = 1;
 };
 
 // block_counts: device scratch of route_sort_workspace_bytes(R, E) bytes
@@ -25,12 +29,16 @@ hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *s
 // Route sort and quant scatter in one launch, for R <= 8192 and top_k <= 16
 // (permute_fused_ok); same outputs as launch_route_sort + launch_quant_scatter.
 bool permute_fused_ok(int R, int top_k);
+// token_major: the quantised tokens go to gmA rows 0..M-1 (row t = token t)
+// instead of to every route's row; pts1 is still written per route row.
 hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, int M, int K, int E,
                                 int top_k, int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
                                 int32_t *sorted_route, int32_t *tokens_per_expert,
-                                int32_t *expert_cumsum, int32_t *err_word, hipStream_t stream);
+                                int32_t *expert_cumsum, int32_t *err_word, bool token_major,
+                                hipStream_t stream);
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
-                                int top_k, int8_t *gmA, float *pts1, hipStream_t stream);
+                                int top_k, int8_t *gmA, float *pts1, bool token_major,
+                                hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,
                                const int32_t *expert_cumsum, int R, int E, int I, int8_t *q2,
                                float *pts2, hipStream_t stream);

@@ -61,7 +61,7 @@ Layout forward_layout(const megamoe_dims &d) {
     L.pts1 = o;   o += align_up(R * 4);
     L.pts2 = o;   o += align_up(R * 4);
     o = align_big(o);
-    L.gmA = o;    o = align_big(o + R * d.K);
+    L.gmA = o;    o = align_big(o + (size_t)d.M * d.K);   // token-major quantised x
     L.gmC = o;    o = align_big(o + R * 2 * d.I * 2);
     L.q2 = o;     o = align_big(o + R * d.I);
     L.g2 = o;     o += align_up(R * d.K * 2);
@@ -77,22 +77,27 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_EHI
         if (_rc != MEGAMOE_OK) return _rc;        \
     } while (0)
 
+// token_major: gmA is [M, K] (row t = quantised token t) rather than the
+// expert-sorted [R, K]; the fused forward reads it through the route list.
 int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_idx, int8_t *gmA,
                 float *pts1, int32_t *eri, int32_t *sorted, int32_t *counts, int32_t *cumsum,
-                int32_t *err_word, int32_t *block_counts, hipStream_t s) {
+                int32_t *err_word, int32_t *block_counts, bool token_major, hipStream_t s) {
     const int R = d.M * d.top_k;
     if (permute_fused_ok(R, d.top_k))
         return hip_status(launch_permute_fused(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA, pts1, eri,
-                                               sorted, counts, cumsum, err_word, s));
+                                               sorted, counts, cumsum, err_word, token_major, s));
     MEGAMOE_TRY(hip_status(launch_route_sort(expert_idx, R, d.E, sorted, eri, counts, cumsum,
                                              err_word, block_counts, s)));
-    return hip_status(launch_quant_scatter(x, eri, d.M, d.K, d.top_k, gmA, pts1, s));
+    return hip_status(
+        launch_quant_scatter(x, eri, d.M, d.K, d.top_k, gmA, pts1, token_major, s));
 }
 
+// a_route (nullable): A row d is token a_route[d] / top_k of a token-major A.
 int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const int8_t *Bp,
-            const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s) {
+            const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s,
+            const int32_t *a_route = nullptr) {
     const int R = d.M * d.top_k;
-    GmmParams prm{A, Bp, scale, cumsum, C, dbg, d.E, N, Kred};
+    GmmParams prm{A, Bp, scale, cumsum, C, dbg, d.E, N, Kred, a_route, d.top_k};
     return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
 }
 
@@ -169,7 +174,7 @@ int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     if (ws_bytes < permute_ws_bytes(*d)) return MEGAMOE_EWORKSPACE;
     return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
                        expert_cumsum, (int32_t *)ws, (int32_t *)((char *)ws + align_up(kErrBytes)),
-                       (hipStream_t)stream);
+                       false, (hipStream_t)stream);
 }
 
 int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert_cumsum,
@@ -241,9 +246,12 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     uint16_t *g2 = (uint16_t *)(base + L.g2);
 
     int32_t *bcnt = (int32_t *)(base + L.bcnt);
-    MEGAMOE_TRY(
-        run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, bcnt, s));
-    MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s));
+    // the quantised tokens are written once, token-major; GMM1 gathers its
+    // expert-sorted rows from them through the route list, so the top_k
+    // copies of each token are never written to or re-read from HBM
+    MEGAMOE_TRY(run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, bcnt,
+                            true, s));
+    MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s, sorted));
     MEGAMOE_TRY(hip_status(
         launch_swiglu_quant(gmC, pts1, cumsum, d->M * d->top_k, d->E, d->I, q2, pts2, s)));
     MEGAMOE_TRY(run_gmm(*d, q2, cumsum, w2p, scale2, g2, nullptr, d->K, d->I, s));

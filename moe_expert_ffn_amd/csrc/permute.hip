@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
 template <int MAXC>
 __global__ __launch_bounds__(256) void quant_scatter_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ expanded_row_idx, int K,
-    int top_k, int8_t *__restrict__ gmA, float *__restrict__ pts1) {
+    int top_k, int8_t *__restrict__ gmA, float *__restrict__ pts1, bool token_major) {
     __shared__ float s_red[4];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -220,9 +220,13 @@ __global__ __launch_bounds__(256) void quant_scatter_kernel(
             packed[j] = word;
         }
         const uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        for (int s = 0; s < top_k; ++s) {
-            const int d = rows[s];
-            if (d >= 0) *reinterpret_cast<uint4 *>(gmA + (size_t)d * K + (size_t)c * 16) = out;
+        if (token_major) {
+            *reinterpret_cast<uint4 *>(gmA + (size_t)t * K + (size_t)c * 16) = out;
+        } else {
+            for (int s = 0; s < top_k; ++s) {
+                const int d = rows[s];
+                if (d >= 0) *reinterpret_cast<uint4 *>(gmA + (size_t)d * K + (size_t)c * 16) = out;
+            }
         }
     }
     if (tid == 0) {
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     int K, int top_k, int8_t *__restrict__ gmA, float *__restrict__ pts1,
     int32_t *__restrict__ expanded_row_idx, int32_t *__restrict__ sorted_route,
     int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_cumsum,
-    int32_t *__restrict__ err_word) {
+    int32_t *__restrict__ err_word, bool token_major) {
     __shared__ int h_all[kMaxExperts + 1];
     __shared__ int h_pre[kMaxExperts + 1];
     __shared__ int s_key[kFusedMaxTopK];
@@ -383,9 +387,13 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
             packed[j] = word;
         }
         const uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        for (int s2 = 0; s2 < top_k; ++s2) {
-            const int d = s_dst[s2];
-            if (d >= 0) *reinterpret_cast<uint4 *>(gmA + (size_t)d * K + (size_t)c * 16) = out;
+        if (token_major) {
+            *reinterpret_cast<uint4 *>(gmA + (size_t)t * K + (size_t)c * 16) = out;
+        } else {
+            for (int s2 = 0; s2 < top_k; ++s2) {
+                const int d = s_dst[s2];
+                if (d >= 0) *reinterpret_cast<uint4 *>(gmA + (size_t)d * K + (size_t)c * 16) = out;
+            }
         }
     }
     if (tid < top_k && s_dst[tid] >= 0) pts1[s_dst[tid]] = scale;
@@ -396,14 +404,15 @@ bool permute_fused_ok(int R, int top_k) { return R <= kFusedMaxR && top_k <= kFu
 hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, int M, int K, int E,
                                 int top_k, int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
                                 int32_t *sorted_route, int32_t *tokens_per_expert,
-                                int32_t *expert_cumsum, int32_t *err_word, hipStream_t stream) {
+                                int32_t *expert_cumsum, int32_t *err_word, bool token_major,
+                                hipStream_t stream) {
     const int R = M * top_k;
     const int per_thread = (K / 16 + 255) / 256;
     dim3 grid(M), block(256);
 #define MEGAMOE_PERMUTE_FUSED(C)                                                              \
     hipLaunchKernelGGL(permute_fused_kernel<C>, grid, block, 0, stream, x, expert_idx, R, E, K, \
                        top_k, gmA, pts1, expanded_row_idx, sorted_route, tokens_per_expert,     \
-                       expert_cumsum, err_word)
+                       expert_cumsum, err_word, token_major)
     if (per_thread <= 1) MEGAMOE_PERMUTE_FUSED(1);
     else if (per_thread <= 2) MEGAMOE_PERMUTE_FUSED(2);
     else if (per_thread <= 4) MEGAMOE_PERMUTE_FUSED(4);
@@ -444,21 +453,22 @@ hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *s
 }
 
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
-                                int top_k, int8_t *gmA, float *pts1, hipStream_t stream) {
+                                int top_k, int8_t *gmA, float *pts1, bool token_major,
+                                hipStream_t stream) {
     const int per_thread = (K / 16 + 255) / 256;
     dim3 grid(M), block(256);
     if (per_thread <= 1)
         hipLaunchKernelGGL(quant_scatter_kernel<1>, grid, block, 0, stream, x, expanded_row_idx, K,
-                           top_k, gmA, pts1);
+                           top_k, gmA, pts1, token_major);
     else if (per_thread <= 2)
         hipLaunchKernelGGL(quant_scatter_kernel<2>, grid, block, 0, stream, x, expanded_row_idx, K,
-                           top_k, gmA, pts1);
+                           top_k, gmA, pts1, token_major);
     else if (per_thread <= 4)
         hipLaunchKernelGGL(quant_scatter_kernel<4>, grid, block, 0, stream, x, expanded_row_idx, K,
-                           top_k, gmA, pts1);
+                           top_k, gmA, pts1, token_major);
     else
         hipLaunchKernelGGL(quant_scatter_kernel<8>, grid, block, 0, stream, x, expanded_row_idx, K,
-                           top_k, gmA, pts1);
+                           top_k, gmA, pts1, token_major);
     return hipGetLastError();
 }
 

@@ -52,8 +52,9 @@ def test_workspace_and_packed_sizes():
     d = MM.dims(2048, 7168, 32, 8, 2048)
     ws = MM.megamoe_workspace_bytes(d)
     R = 2048 * 8
-    # intermediates: gmA + gmC + q2 + gmm2_out dominate
-    assert ws >= R * 7168 + R * 4096 * 2 + R * 2048 + R * 7168 * 2
+    # intermediates: the token-major quantised x [M, K] plus gmC + q2 +
+    # gmm2_out, all [R, .], dominate
+    assert ws >= 2048 * 7168 + R * 4096 * 2 + R * 2048 + R * 7168 * 2
     assert ws < R * 7168 * 6
     assert MM.megamoe_packed_weight_bytes(d) == (32 * 7168 * 4096, 32 * 2048 * 7168)
     # the packed layout pads each expert's output columns to whole 256-row blocks
