@@ -11,10 +11,11 @@ untimed calls (the clocks of an idle GPU take that long to settle under load),
 W untimed steps, then K timed steps enqueued back to back between two device
 synchronisations.  The
 per-stage durations (and the roofline of the dominant kernel) come from a
-second timed loop of K steps that calls the per-stage entry points of the C
-ABI -- the same kernels, in the same order, as megamoe_forward -- with HIP
-events recorded on the launch stream between the stages (the event records
-cost a little, so that loop's step time is reported separately).  The forward
+second timed loop of K steps that calls the stage entry points megamoe_forward
+is made of (megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
+megamoe_gmm2, megamoe_unpermute) -- the same kernels, in the same order --
+with HIP events recorded on the launch stream between the stages (the event
+records cost a little, so that loop's step time is reported separately).  The forward
 captured into a HIP graph and replayed is timed as well.
 """
 from __future__ import annotations
@@ -64,9 +65,10 @@ def algorithmic(w, counts: np.ndarray) -> dict:
     act = int(np.count_nonzero(counts))
     b = {}
     # sort reads expert ids, writes 2 index arrays + counts; quant reads x once,
-    # writes topK int8 rows + scales
-    b["permute"] = R * 4 + 2 * R * 4 + 2 * E * 4 + w.M * K * 2 + R * K + R * 4
-    b["gmm1"] = act * K * 2 * I + R * K + R * 2 * I * 2 + E * 2 * I * 4
+    # writes each token's int8 row once (token-major) + a scale per route
+    b["permute"] = R * 4 + 2 * R * 4 + 2 * E * 4 + w.M * K * 2 + w.M * K + R * 4
+    # GMM1 gathers its rows from the token-major int8 x through the route list
+    b["gmm1"] = act * K * 2 * I + w.M * K + R * 4 + R * 2 * I * 2 + E * 2 * I * 4
     b["swiglu"] = R * 2 * I * 2 + R * 4 + R * I + R * 4
     b["gmm2"] = act * I * K + R * I + R * K * 2 + E * K * 4
     b["unpermute"] = R * K * 2 + R * 4 + R * 4 + R * 4 + w.M * K * 2
@@ -277,7 +279,7 @@ def main():
 
     R = w.R
     f = dict(device="cuda")
-    gmA = torch.empty((R, w.K), dtype=torch.int8, **f)
+    qx = torch.empty((w.M, w.K), dtype=torch.int8, **f)
     pts1 = torch.empty(R, dtype=torch.float32, **f)
     eri = torch.empty(R, dtype=torch.int32, **f)
     srt = torch.empty(R, dtype=torch.int32, **f)
@@ -295,10 +297,11 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        MM.megamoe_permute(d, dev["x"], dev["expert_idx"], gmA, pts1, eri, srt, cnt, cum, pws)
+        MM.megamoe_permute_tokens(d, dev["x"], dev["expert_idx"], qx, pts1, eri, srt, cnt, cum,
+                                  pws)
         if ev is not None:
             ev[1].record(stream)
-        MM.megamoe_gmm1(d, gmA, cum, w1p, dev["scale1"], gmC)
+        MM.megamoe_gmm1_gather(d, qx, srt, cum, w1p, dev["scale1"], gmC)
         if ev is not None:
             ev[2].record(stream)
         MM.megamoe_swiglu_quant(d, gmC, pts1, cum, q2, pts2)

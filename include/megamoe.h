@@ -86,10 +86,10 @@ int megamoe_prepack_w2(const megamoe_dims *d, const int8_t *w2, int8_t *w2p, voi
  *   out        bf16  [M, K]
  *   workspace  >= megamoe_workspace_bytes(); the caller may not touch it while
  *              the forward runs.  Intermediates live there.
- * The result equals, bit for bit, that of the five stage entry points below
- * run in order.  Internally the forward keeps the quantised tokens token-major
- * ([M, K], each written once) and GMM1 gathers its expert-sorted rows from
- * them through the route list, instead of materialising the [R, K] gmA. */
+ * It runs megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
+ * megamoe_gmm2 and megamoe_unpermute in order on the workspace; the result
+ * equals, bit for bit, that of the page's five stages (megamoe_permute and
+ * megamoe_gmm1 in place of the first two). */
 int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
                     const float *probs, const int8_t *w1p, const float *scale1,
                     const int8_t *w2p, const float *scale2, uint16_t *out,
@@ -111,6 +111,18 @@ int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
                     int32_t *tokens_per_expert, int32_t *expert_cumsum, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Stage 1 as megamoe_forward runs it: the same sort outputs and pts1 as
+ * megamoe_permute, but each token's quantised row is written once,
+ * token-major, instead of to every route's row:
+ *   qx  int8 [M, K]   qx[t] = the int8 row of token t; gmA[row] of
+ *                     megamoe_permute equals qx[sorted_route[row] / top_k]
+ * The other arguments are those of megamoe_permute. */
+int megamoe_permute_tokens(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                           int8_t *qx, float *pts1, int32_t *expanded_row_idx,
+                           int32_t *sorted_route, int32_t *tokens_per_expert,
+                           int32_t *expert_cumsum, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* Stage 3 GMM1, section 3: for every row of expert e's group,
  *   acc[row, n] = sum_k gmA[row, k] * w1[e, k, n]   (int32, exact)
  *   gmC[row, n] = fp16(fp32(acc) * scale1[e, n])
@@ -119,6 +131,17 @@ int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
 int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert_cumsum,
                  const int8_t *w1p, const float *scale1, uint16_t *gmC, int32_t *acc_dbg,
                  void *stream);
+
+/* GMM1 as megamoe_forward runs it: the A row of sorted row `row` is read
+ * from qx[sorted_route[row] / top_k] (qx from megamoe_permute_tokens), so the
+ * expert-sorted gmA is never materialised.  Results equal those of
+ * megamoe_gmm1 on that gmA bit for bit.
+ *   qx            int8  [M, K]
+ *   sorted_route  int32 [R]    from the same permute call
+ * The other arguments are those of megamoe_gmm1. */
+int megamoe_gmm1_gather(const megamoe_dims *d, const int8_t *qx, const int32_t *sorted_route,
+                        const int32_t *expert_cumsum, const int8_t *w1p, const float *scale1,
+                        uint16_t *gmC, int32_t *acc_dbg, void *stream);
 
 /* Stage 4 SwiGLU, section 4: per valid row,
  *   c = fp32(gmC) * pts1;  y = silu(c[0:I]) * c[I:2I];  pts2 = max|y| / 127;

@@ -101,6 +101,21 @@ int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const
     return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
 }
 
+int permute_entry(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                  int8_t *gmA, float *pts1, int32_t *eri, int32_t *sorted_route,
+                  int32_t *tokens_per_expert, int32_t *expert_cumsum, void *ws, size_t ws_bytes,
+                  bool token_major, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
+                          expert_cumsum, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (ws_bytes < permute_ws_bytes(*d)) return MEGAMOE_EWORKSPACE;
+    return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
+                       expert_cumsum, (int32_t *)ws, (int32_t *)((char *)ws + align_up(kErrBytes)),
+                       token_major, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,15 +181,16 @@ int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
                     int8_t *gmA, float *pts1, int32_t *eri, int32_t *sorted_route,
                     int32_t *tokens_per_expert, int32_t *expert_cumsum, void *ws,
                     size_t ws_bytes, void *stream) {
-    MEGAMOE_TRY(megamoe_check_dims(d));
-    const void *ptrs[] = {x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
-                          expert_cumsum, ws};
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return MEGAMOE_EINVAL;
-    if (ws_bytes < permute_ws_bytes(*d)) return MEGAMOE_EWORKSPACE;
-    return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
-                       expert_cumsum, (int32_t *)ws, (int32_t *)((char *)ws + align_up(kErrBytes)),
-                       false, (hipStream_t)stream);
+    return permute_entry(d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
+                         expert_cumsum, ws, ws_bytes, false, stream);
+}
+
+int megamoe_permute_tokens(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                           int8_t *qx, float *pts1, int32_t *eri, int32_t *sorted_route,
+                           int32_t *tokens_per_expert, int32_t *expert_cumsum, void *ws,
+                           size_t ws_bytes, void *stream) {
+    return permute_entry(d, x, expert_idx, qx, pts1, eri, sorted_route, tokens_per_expert,
+                         expert_cumsum, ws, ws_bytes, true, stream);
 }
 
 int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert_cumsum,
@@ -187,6 +203,18 @@ int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert
     if (acc_dbg && !aligned16(acc_dbg)) return MEGAMOE_EINVAL;
     return run_gmm(*d, gmA, expert_cumsum, w1p, scale1, gmC, acc_dbg, 2 * d->I, d->K,
                    (hipStream_t)stream);
+}
+
+int megamoe_gmm1_gather(const megamoe_dims *d, const int8_t *qx, const int32_t *sorted_route,
+                        const int32_t *expert_cumsum, const int8_t *w1p, const float *scale1,
+                        uint16_t *gmC, int32_t *acc_dbg, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {qx, sorted_route, expert_cumsum, w1p, scale1, gmC};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (acc_dbg && !aligned16(acc_dbg)) return MEGAMOE_EINVAL;
+    return run_gmm(*d, qx, expert_cumsum, w1p, scale1, gmC, acc_dbg, 2 * d->I, d->K,
+                   (hipStream_t)stream, sorted_route);
 }
 
 int megamoe_swiglu_quant(const megamoe_dims *d, const uint16_t *gmC, const float *pts1,

@@ -36,8 +36,8 @@ class megamoe_dims(ctypes.Structure):
 EXPORTED = [
     "megamoe_strerror", "megamoe_check_dims", "megamoe_workspace_bytes",
     "megamoe_permute_workspace_bytes", "megamoe_packed_weight_bytes", "megamoe_prepack_w1",
-    "megamoe_prepack_w2", "megamoe_forward", "megamoe_permute", "megamoe_gmm1",
-    "megamoe_swiglu_quant", "megamoe_gmm2", "megamoe_unpermute", "megamoe_last_error",
+    "megamoe_prepack_w2", "megamoe_forward", "megamoe_permute", "megamoe_permute_tokens",
+    "megamoe_gmm1", "megamoe_gmm1_gather", "megamoe_swiglu_quant", "megamoe_gmm2", "megamoe_unpermute", "megamoe_last_error",
 ]
 
 _lib = None
@@ -67,7 +67,11 @@ def load() -> ctypes.CDLL:
     L.megamoe_forward.restype = i32
     L.megamoe_permute.argtypes = [D, P, P, P, P, P, P, P, P, P, sz, P]
     L.megamoe_permute.restype = i32
+    L.megamoe_permute_tokens.argtypes = [D, P, P, P, P, P, P, P, P, P, sz, P]
+    L.megamoe_permute_tokens.restype = i32
     L.megamoe_gmm1.argtypes, L.megamoe_gmm1.restype = [D, P, P, P, P, P, P, P], i32
+    L.megamoe_gmm1_gather.argtypes = [D, P, P, P, P, P, P, P, P]
+    L.megamoe_gmm1_gather.restype = i32
     L.megamoe_swiglu_quant.argtypes = [D, P, P, P, P, P, P]
     L.megamoe_swiglu_quant.restype = i32
     L.megamoe_gmm2.argtypes, L.megamoe_gmm2.restype = [D, P, P, P, P, P, P, P], i32
@@ -162,6 +166,24 @@ def megamoe_permute(d, x, expert_idx, gmA, pts1, expanded_row_idx, sorted_route,
         _ptr(sorted_route, torch.int32), _ptr(tokens_per_expert, torch.int32),
         _ptr(expert_cumsum, torch.int32), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def megamoe_permute_tokens(d, x, expert_idx, qx, pts1, expanded_row_idx, sorted_route,
+                           tokens_per_expert, expert_cumsum, workspace, stream=None):
+    _check("megamoe_permute_tokens", load().megamoe_permute_tokens(
+        ctypes.byref(d), _ptr(x, torch.float16), _ptr(expert_idx, torch.int32),
+        _ptr(qx, torch.int8), _ptr(pts1, torch.float32), _ptr(expanded_row_idx, torch.int32),
+        _ptr(sorted_route, torch.int32), _ptr(tokens_per_expert, torch.int32),
+        _ptr(expert_cumsum, torch.int32), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def megamoe_gmm1_gather(d, qx, sorted_route, expert_cumsum, w1p, scale1, gmC, acc_dbg=None,
+                        stream=None):
+    _check("megamoe_gmm1_gather", load().megamoe_gmm1_gather(
+        ctypes.byref(d), _ptr(qx, torch.int8), _ptr(sorted_route, torch.int32),
+        _ptr(expert_cumsum, torch.int32), _ptr(w1p, torch.int8), _ptr(scale1, torch.float32),
+        _ptr(gmC, torch.float16), _ptr(acc_dbg, torch.int32), _stream(stream)))
 
 
 def megamoe_gmm1(d, gmA, expert_cumsum, w1p, scale1, gmC, acc_dbg=None, stream=None):

@@ -28,8 +28,12 @@ def prepack(d, dev: dict):
     return w1p, w2p
 
 
-def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True) -> dict:
-    """Each stage through its own entry point; every intermediate returned (device)."""
+def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True, gather: bool = False) -> dict:
+    """Each stage through its own entry point; every intermediate returned (device).
+
+    gather: the first two stages as the forward runs them
+    (megamoe_permute_tokens + megamoe_gmm1_gather); o["qx"] then holds the
+    token-major quantised x and o["gmA"] stays zero."""
     d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
     R = w.R
     cu = dict(device="cuda")
@@ -50,11 +54,19 @@ def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True) -> dict:
         o["acc1"] = torch.zeros((R, w.N1), dtype=torch.int32, **cu)
         o["acc2"] = torch.zeros((R, w.K), dtype=torch.int32, **cu)
     ws = torch.empty(MM.megamoe_permute_workspace_bytes(d), dtype=torch.uint8, **cu)
-    MM.megamoe_permute(d, dev["x"], dev["expert_idx"], o["gmA"], o["pts1"],
-                       o["expanded_row_idx"], o["sorted_route"], o["tokens_per_expert"],
-                       o["expert_cumsum"], ws)
-    MM.megamoe_gmm1(d, o["gmA"], o["expert_cumsum"], w1p, dev["scale1"], o["gmC"],
-                    o.get("acc1"))
+    if gather:
+        o["qx"] = torch.zeros((w.M, w.K), dtype=torch.int8, **cu)
+        MM.megamoe_permute_tokens(d, dev["x"], dev["expert_idx"], o["qx"], o["pts1"],
+                                  o["expanded_row_idx"], o["sorted_route"],
+                                  o["tokens_per_expert"], o["expert_cumsum"], ws)
+        MM.megamoe_gmm1_gather(d, o["qx"], o["sorted_route"], o["expert_cumsum"], w1p,
+                               dev["scale1"], o["gmC"], o.get("acc1"))
+    else:
+        MM.megamoe_permute(d, dev["x"], dev["expert_idx"], o["gmA"], o["pts1"],
+                           o["expanded_row_idx"], o["sorted_route"], o["tokens_per_expert"],
+                           o["expert_cumsum"], ws)
+        MM.megamoe_gmm1(d, o["gmA"], o["expert_cumsum"], w1p, dev["scale1"], o["gmC"],
+                        o.get("acc1"))
     MM.megamoe_swiglu_quant(d, o["gmC"], o["pts1"], o["expert_cumsum"], o["q2"], o["pts2"])
     MM.megamoe_gmm2(d, o["q2"], o["expert_cumsum"], w2p, dev["scale2"], o["gmm2_out"],
                     o.get("acc2"))

@@ -97,6 +97,23 @@ def test_stages_and_forward_small(w):
     g_fast = H.run_stages(w, dev, w1p, w2p, debug_acc=False)
     for k in ("gmC", "gmm2_out"):
         assert torch.equal(g_fast[k].view(torch.int16), g[k].view(torch.int16)), k
+    _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+
+
+def _compare_gather(w, g, gg):
+    """The forward's first two stages (token-major quantised x, GMM1 gathering
+    its rows through the route list) against the page's (gmA scattered to
+    every route's row): the same bits everywhere."""
+    for k in ("sorted_route", "expanded_row_idx", "tokens_per_expert", "expert_cumsum"):
+        assert torch.equal(gg[k], g[k]), k
+    Rv = int(g["expert_cumsum"][-1].item()) if w.E else 0
+    srt = g["sorted_route"][:Rv].long()
+    assert torch.equal(gg["qx"][srt // w.top_k], g["gmA"][:Rv]), "qx rows vs gmA"
+    assert torch.equal(gg["pts1"][:Rv], g["pts1"][:Rv]), "pts1"
+    assert torch.equal(gg["acc1"][:Rv], g["acc1"][:Rv]), "acc1"
+    for k in ("gmC", "q2", "gmm2_out"):
+        assert torch.equal(gg[k][:Rv].view(torch.int8), g[k][:Rv].view(torch.int8)), k
+    assert torch.equal(gg["out"].view(torch.int16), g["out"].view(torch.int16)), "out"
 
 
 def test_hot_expert_and_duplicates():
@@ -184,6 +201,8 @@ def test_full_size_sampled(name):
     for k in ("gmC", "gmm2_out"):
         assert torch.equal(g_fast[k].view(torch.int16), g[k].view(torch.int16)), k
     del g_fast
+    # the forward's gathered GMM1 equals the page's staged GMM1
+    _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
 
     # sort metadata: bit-exact everywhere
     srt = O.route_sort(inp["expert_idx"], w.E)
