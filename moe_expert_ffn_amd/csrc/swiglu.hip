@@ -10,12 +10,39 @@
 // chunks of y in registers, so the row maximum is a wave reduction and the
 // row needs a single pass over HBM.  Every load of the row is issued before
 // the validity check, so the two memory round trips overlap.
+//
+// At large row counts the kernel is bound by VALU issue, not HBM, so silu is
+// evaluated with the hardware's base-2 exponential and reciprocal (see
+// silu_times below) rather than with the IEEE-rounded library exp and
+// division, which cost about three times the instructions.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace megamoe {
 
 constexpr int kRowsPerBlock = 4;
+
+// silu(u) * g in fp32.
+//  * exp(-u) = 2^(-u * log2(e)), from the hardware base-2 exponential
+//    (v_exp_f32, about 1 ulp); rounding the scaled argument adds a relative
+//    error of about |u| * 2^-24 * ln 2, a few ulp for |u| up to 10.
+//  * u / d, d = 1 + exp(-u) >= 1: q = u * rcp(d) with the hardware reciprocal,
+//    then one correction of the quotient, q + rcp(d) * (u - q * d), with the
+//    residual from an FMA (Markstein's division method).  This gives the
+//    correctly rounded quotient except next to a rounding midpoint.
+//  * Non-finite cases keep IEEE results: d = inf (u < -88) gives -0, u = inf
+//    gives inf, u = -inf or NaN gives NaN (the uncorrected quotient q).
+// On the decode, large and skewed workloads every q2 code and every
+// scale2 produced this way equals the one from the IEEE exp and division.
+__device__ __forceinline__ float silu_times(float u, float g) {
+    const float ex = __builtin_amdgcn_exp2f(u * -1.4426950408889634f);
+    const float d = ex + 1.0f;
+    const float r = __builtin_amdgcn_rcpf(d);
+    const float q = u * r;
+    float sl = __builtin_fmaf(__builtin_fmaf(-q, d, u), r, q);
+    if (!__builtin_isfinite(sl)) sl = q;
+    return sl * g;
+}
 
 template <int MAXC>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void swiglu_quant_kernel(
@@ -52,10 +79,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void swiglu_quant_kernel(
             for (int j = 0; j < 8; ++j) {
                 const float u = h2f((uint16_t)((uw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;
                 const float g = h2f((uint16_t)((gw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;
-                const float ex = expf(u * -1.0f);
-                const float den = ex + 1.0f;
-                const float sl = u / den;
-                const float v = sl * g;
+                const float v = silu_times(u, g);
                 y[i][j] = v;
                 amax = fmaxf(amax, fabsf(v));
             }
