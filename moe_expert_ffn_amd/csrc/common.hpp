@@ -28,17 +28,20 @@ __device__ __forceinline__ float keep_f32(float v) {
     return v;
 }
 
-// fp32 -> bf16 bits, round to nearest even.  Adding 0x7fff plus the lowest kept
-// bit and truncating rounds half-way cases to the even neighbour; overflow
-// carries into the exponent and yields infinity.  NaNs stay quiet NaNs.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 values -> packed bf16 bits (a in the low half), round to nearest
+// even, by the gfx950 conversion instruction v_cvt_pk_bf16_f32.  Over all 2^32
+// fp32 bit patterns it gives the same bits as rounding the pattern in integer
+// arithmetic (add 0x7fff plus the lowest kept bit, truncate; overflow carries
+// into infinity), with every NaN kept a NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf_pk(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
-__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+// bf16 bits in the low / high half of a word -> fp32 (exact)
+__device__ __forceinline__ float bf2f_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -56,17 +56,19 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
             if (d[u] < 0) continue;
             const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[u]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float g = h2f((uint16_t)((w[j >> 1] >> ((j & 1) * 16)) & 0xffffu));
-                const float deq = bf2f(f2bf(g * sc[u]));  // combine: cast to the output type
-                const float weighted = deq * p[u];
-                acc[j] = acc[j] + weighted;
+            for (int j = 0; j < 8; j += 2) {
+                const float g0 = h2f((uint16_t)(w[j >> 1] & 0xffffu));
+                const float g1 = h2f((uint16_t)(w[j >> 1] >> 16));
+                // combine: cast the dequantised row to the output type
+                const uint32_t deq = f2bf_pk(g0 * sc[u], g1 * sc[u]);
+                acc[j] = acc[j] + bf2f_lo(deq) * p[u];
+                acc[j + 1] = acc[j + 1] + bf2f_hi(deq) * p[u];
             }
         }
     }
     uint32_t o[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = f2bf(acc[2 * j]) | (f2bf(acc[2 * j + 1]) << 16);
+    for (int j = 0; j < 4; ++j) o[j] = f2bf_pk(acc[2 * j], acc[2 * j + 1]);
     *reinterpret_cast<uint4 *>(out + (size_t)t * K + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
