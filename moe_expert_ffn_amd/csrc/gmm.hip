@@ -214,8 +214,15 @@ __device__ __forceinline__ void store_tile_lds(const GmmParams &p, const v4i (&a
     }
 }
 
-template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true>
+template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true, int PRIO = 0>
 __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
+    // PRIO > 0 (two workgroups per CU that stream weights): the older of the
+    // two workgroups on a CU wins the CU's arbitration, and with equal work
+    // it was measured to finish up to 25% before its partner, which then
+    // streams alone at half the copies in flight.  The two alternate their
+    // wave priority every PRIO K steps in opposite phase; the grid's first
+    // and second halves are the dispatcher's first and second workgroup on
+    // each CU.
     constexpr int BN = kPackRows;
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -253,6 +260,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         !TRIM ? per_xcd : rounds ? min(per_xcd, ((total + rounds - 1) / rounds + 7) >> 3) : 0;
     if ((int)(blockIdx.x >> 3) >= act_xcd) return;
     const int G = act_xcd << 3;
+    [[maybe_unused]] const int late = (int)blockIdx.x >= (int)(gridDim.x >> 1);
     const int vid = (blockIdx.x & 7) * act_xcd + (blockIdx.x >> 3);
     const int wm0 = (wave / WAVES_N) * WM;
     const int wn0 = (wave % WAVES_N) * WN;
@@ -384,6 +392,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 static_for<0, 2>([&](auto uc) {
                     constexpr int cur = decltype(uc)::value, nxt = cur ^ 1;
                     const int kt = kt0 + cur;
+                    if constexpr (PRIO > 0 && cur == 0) {
+                        static_assert(PRIO % 2 == 0, "kt is even here");
+                        if (kt % PRIO == 0) {
+                            if (((kt / PRIO) & 1) ^ late) __builtin_amdgcn_s_setprio(2);
+                            else __builtin_amdgcn_s_setprio(0);
+                        }
+                    }
                     // stage kt+1 must have landed; stages up to kt+NS-1 were
                     // issued, the NS-2 after kt+1 may be in flight
                     if (kt + NS - 1 < nst) wait_vmcnt<(NS - 2) * LPW>();
@@ -452,7 +467,8 @@ hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipS
 // interleaved repetitions):
 //  * few rows per expert: the GEMM streams weights (HBM bound); a 64-row tile
 //    with a 3-stage ring fits twice per CU, so two workgroups per CU keep
-//    twice the copies in flight;
+//    twice the copies in flight, and they alternate priority every 16 K
+//    steps so that neither finishes long after the other;
 //  * more rows: MFMA bound; 256 x 256 tiles on 16 waves (64 x 64 per wave),
 //    which beat 8-wave layouts of the same tile on every shape measured.
 // ---------------------------------------------------------------------------
@@ -464,7 +480,7 @@ struct GmmVariant {
 };
 
 static GmmVariant g_variants[] = {
-    {64, 256, gmm_i8_ring_kernel<64, 1, 4, 3, true>, 256, 0},
+    {64, 256, gmm_i8_ring_kernel<64, 1, 4, 3, true, true, 16>, 256, 0},
     {256, 256, gmm_i8_ring_kernel<256, 4, 4, 4, false>, 1024, 0},
 };
 
