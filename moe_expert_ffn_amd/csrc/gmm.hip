@@ -279,16 +279,19 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     }
 
     // Tiles vid, vid + G, ... for the F full rounds.  When the last round is
-    // sparse (L <= G / 4 tiles), its tiles go to the workgroups whose full
-    // rounds cost least (live row blocks summed over their tiles; ties by
-    // position): every workgroup computes all G costs and its own rank the same
-    // way.  Tiles of unequal cost (ragged groups) otherwise leave the few
-    // workgroups of that round finishing long after the rest.  A fuller last
-    // round keeps the plain order, whose adjacent tiles share L2 data.
+    // sparse (L <= G / 4 tiles), each of its tiles is cut into WAVES_N column
+    // pieces (one wave column each) and the WAVES_N * L pieces go to the
+    // workgroups whose full rounds cost least (live row blocks summed over
+    // their tiles; ties by position): every workgroup computes all G costs and
+    // its own rank the same way.  A piece streams its tile's copies but only
+    // the waves of its columns multiply and store, so a leftover tile no
+    // longer keeps one workgroup busy for a whole tile after the rest are
+    // done.  A fuller last round keeps the plain order, whose adjacent tiles
+    // share L2 data.
     __shared__ int s_cost[kMaxWorkgroups];
-    __shared__ int s_extra;
+    __shared__ int s_extra, s_piece;
     const int F = total / G, L = total - F * G;
-    const bool ranked = !TRIM && L > 0 && 4 * L <= G;
+    const bool ranked = !TRIM && L > 0 && WAVES_N * L <= G;
     if (ranked) {
         for (int w = tid; w < G; w += NW * kWave) {
             int c = 0;
@@ -304,11 +307,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             const int mine = s_cost[vid];
             int rank = 0;
             for (int w = 0; w < G; ++w) rank += s_cost[w] < mine || (s_cost[w] == mine && w < vid);
-            s_extra = rank < L ? F * G + rank : -1;
+            s_extra = rank < WAVES_N * L ? F * G + rank / WAVES_N : -1;
+            s_piece = rank % WAVES_N;
         }
         __syncthreads();
     }
     const int extra = ranked ? s_extra : (vid < L ? F * G + vid : -1);
+    const int piece = ranked ? s_piece : 0;
 
     int parity = 0;
     for (int k = 0;; ++k, parity ^= 1) {
@@ -416,12 +421,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 });
             }
         };
-        if (!SKIP || wm0 < rows) kloop(std::true_type{});
+        // a column piece of a leftover tile: only its wave column multiplies
+        // and stores (the other pieces of the tile run on other workgroups)
+        const bool col_live = !ranked || k < F || wave % WAVES_N == piece;
+        if ((!SKIP || wm0 < rows) && col_live) kloop(std::true_type{});
         else kloop(std::false_type{});
 
         // every copy of the tile has been awaited inside the loop (the scale
         // copy is older than all of them), and the last barrier published them
-        store_tile_lds<TM, TN>(p, acc, s_scale[parity], row0, rows, n0, wm0, wn0, lane);
+        if (col_live)
+            store_tile_lds<TM, TN>(p, acc, s_scale[parity], row0, rows, n0, wm0, wn0, lane);
     }
 }
 

@@ -129,6 +129,37 @@ def test_hot_expert_and_duplicates():
     _compare_full(w, inp, o_ref, g)
 
 
+def test_leftover_tiles_split_by_columns():
+    """The 256-row GEMM configuration with one full round of tiles and a
+    sparse last round: 256 experts, 20 of them with 300 rows (two m-blocks)
+    and 236 with 130 rows, K = 256 and I = 128 (one n-block in both GEMMs),
+    so each GEMM has 276 tiles for 256 workgroups.  The 20 leftover tiles are
+    cut into column pieces run by different workgroups; every output element
+    is compared with the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hot, cold, E = 20, 236, 256
+    M = hot * 300 + cold * 130
+    w = W.custom(M, 256, E, 1, 128, name="leftover_tiles")
+    tiles = hot * 2 + cold
+    G = (min(cus, M // 256 + E) + 7) // 8 * 8      # the launch grid of the GEMM
+    F, L = tiles // G, tiles % G
+    assert F >= 1 and 1 <= L and 4 * L <= G, f"shape does not reach the split path on {cus} CUs"
+    print(f"[parity] {w.describe()} tiles {tiles} on {G} workgroups", flush=True)
+    inp = W.generate(w, seed=4)
+    ids = np.concatenate([np.repeat(np.arange(hot), 300), hot + np.repeat(np.arange(cold), 130)])
+    inp["expert_idx"][:, 0] = np.random.default_rng(5).permutation(ids).astype(np.int32)
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    out, dropped = H.run_forward(w, dev, w1p, w2p)
+    assert dropped == 0
+    assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
+
+
 def test_dropped_routes_error_word():
     w = W.custom(40, 256, 8, 3, 128, name="dropped")
     inp = W.generate(w, seed=2)
