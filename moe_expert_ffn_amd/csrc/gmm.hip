@@ -45,13 +45,28 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-// Builds the per-expert tile prefix in LDS (wave 0) and returns the tile count.
-template <int BM>
-__device__ __forceinline__ int build_tile_prefix(const GmmParams &p, int NB, int *s_tile_start,
-                                                 int *s_row_off, int *s_rows) {
+// Tile schedule.  Expert e's rows are split over its m-blocks =
+// ceil(rows / BM) as evenly as whole units (UNIT rows, one wave row block)
+// allow -- 530 rows become 192 + 192 + 146, not 256 + 256 + 18, since a ragged
+// last block would stream a full tile's weights for a fraction of the MFMA
+// work.  With nu = ceil(rows / UNIT) units, the first ur = nu % mb m-blocks get
+// uq + 1 units and the rest uq = nu / mb.  A tile's cost class is its unit
+// count c in 1..U (U = BM / UNIT), which its MFMA time follows.
+//
+// Tiles are numbered cost class by cost class, the largest first; inside a
+// class by expert, then n-block, then m-block, so the m-blocks that share a
+// weight block stay adjacent.  s_pre[c - 1][e] counts the tiles of class c of
+// the experts before e (s_pre[c - 1][E]: all of class c).  With U = 1 this is
+// the plain expert / n-block / m-block order.
+template <int BM, int UNIT>
+__device__ __forceinline__ int build_schedule(const GmmParams &p, int NB, int (*s_pre)[kMaxE + 1],
+                                              int *s_row_off, int *s_rows) {
+    constexpr int U = BM / UNIT;
     const int lane = threadIdx.x & (kWave - 1);
     if ((threadIdx.x >> 6) == 0) {
-        int run = 0;
+        int run[U];
+#pragma unroll
+        for (int c = 0; c < U; ++c) run[c] = 0;
         for (int base = 0; base < p.E; base += kWave) {
             const int e = base + lane;
             int rows = 0, off = 0;
@@ -60,45 +75,67 @@ __device__ __forceinline__ int build_tile_prefix(const GmmParams &p, int NB, int
                 off = e ? p.cumsum[e - 1] : 0;
                 rows = hi - off;
             }
-            const int tiles = ((rows + BM - 1) / BM) * NB;
-            const int incl = wave_inclusive_scan(tiles);
+            const int mb = (rows + BM - 1) / BM;
+            const int nu = (rows + UNIT - 1) / UNIT;
+            const int uq = mb ? nu / mb : 0, ur = mb ? nu - uq * mb : 0;
+#pragma unroll
+            for (int c = 1; c <= U; ++c) {
+                const int blocks = (c == uq + 1 ? ur : 0) + (c == uq ? mb - ur : 0);
+                const int tiles = blocks * NB;
+                const int incl = wave_inclusive_scan(tiles);
+                if (e < p.E) s_pre[c - 1][e] = run[c - 1] + incl - tiles;
+                run[c - 1] += __shfl(incl, kWave - 1, kWave);
+            }
             if (e < p.E) {
-                s_tile_start[e] = run + incl - tiles;
                 s_row_off[e] = off;
                 s_rows[e] = rows;
             }
-            run += __shfl(incl, kWave - 1, kWave);
         }
-        if (lane == 0) s_tile_start[p.E] = run;
+        if (lane == 0) {
+#pragma unroll
+            for (int c = 0; c < U; ++c) s_pre[c][p.E] = run[c];
+        }
     }
     __syncthreads();
-    return s_tile_start[p.E];
+    int total = 0;
+#pragma unroll
+    for (int c = 0; c < U; ++c) total += s_pre[c][p.E];
+    return total;
 }
 
-// Rows of tile t, from the LDS tile prefix: expert e's rows are split over its
-// m-blocks as evenly as whole units (one wave row block each) allow -- 530 rows
-// become 192 + 192 + 146, not 256 + 256 + 18, since a ragged last block would
-// stream a full tile's weights for a fraction of the MFMA work.  Tiles of one
-// expert are ordered n-block-major, m-blocks innermost.
+// Cost class of tile t (largest class first in the numbering)
+template <int U>
+__device__ __forceinline__ int tile_class(int t, int E, const int (*s_pre)[kMaxE + 1]) {
+    int c = U;
+    while (c > 1 && t >= s_pre[c - 1][E]) t -= s_pre[--c][E];
+    return c;
+}
+
 struct TileRows {
     int e, row0, rows, nblk;
 };
 template <int BM, int UNIT>
-__device__ __forceinline__ TileRows tile_rows(int t, int E, const int *s_tile_start,
+__device__ __forceinline__ TileRows tile_rows(int t, int E, const int (*s_pre)[kMaxE + 1],
                                               const int *s_row_off, const int *s_rows) {
-    int lo = 0, hi = E - 1;
+    constexpr int U = BM / UNIT;
+    int c = U;
+    while (c > 1 && t >= s_pre[c - 1][E]) t -= s_pre[--c][E];
+    const int *pre = s_pre[c - 1];
+    int lo = 0, hi = E - 1;  // last expert whose class-c tiles start at or before t
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_tile_start[mid] <= t) lo = mid;
+        if (pre[mid] <= t) lo = mid;
         else hi = mid - 1;
     }
     const int rows_e = s_rows[lo];
     const int mb = (rows_e + BM - 1) / BM;
-    const int local = t - s_tile_start[lo];
-    const int nblk = local / mb;
-    const int mblk = local - nblk * mb;
     const int nu = (rows_e + UNIT - 1) / UNIT;
     const int uq = nu / mb, ur = nu - uq * mb;
+    const bool upper = ur > 0 && c == uq + 1;  // the first ur m-blocks
+    const int m = upper ? ur : mb - ur;        // m-blocks of this class
+    const int local = t - pre[lo];
+    const int nblk = local / m;
+    const int mblk = (upper ? 0 : ur) + (local - nblk * m);
     const int first = UNIT * (mblk * uq + min(mblk, ur));
     const int last = min(rows_e, UNIT * ((mblk + 1) * uq + min(mblk + 1, ur)));
     return TileRows{lo, s_row_off[lo] + first, last - first, nblk};
@@ -237,7 +274,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
 
     __shared__ __attribute__((aligned(1024))) int8_t smem[NS * kStage];
     __shared__ __attribute__((aligned(16))) float s_scale[2][BN];
-    __shared__ int s_tile_start[kMaxE + 1];
+    constexpr int U = WAVES_M;                       // cost classes (live row blocks)
+    __shared__ int s_pre[U][kMaxE + 1];
     __shared__ int s_row_off[kMaxE];
     __shared__ int s_rows[kMaxE];
 
@@ -246,7 +284,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     const int wave = tid >> 6;
     const int N = p.N, Kred = p.Kred;
     const int NB = (N + BN - 1) / BN;
-    const int total = build_tile_prefix<BM>(p, NB, s_tile_start, s_row_off, s_rows);
+    const int total = build_schedule<BM, BM / WAVES_M>(p, NB, s_pre, s_row_off, s_rows);
 
     // TRIM (active grid, for tiles of equal cost that stream weights): with
     // k = ceil(total / gridDim) tiles for the busiest workgroup, ceil(total / k)
@@ -278,48 +316,40 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             fb_off[j] = BM * kBK64 + lds_off64s(wn0 + 16 * j + (lane & 15), chunk);
     }
 
-    // Tiles vid, vid + G, ... for the F full rounds.  When the last round is
-    // sparse (L <= G / 4 tiles), each of its tiles is cut into WAVES_N column
-    // pieces (one wave column each) and the WAVES_N * L pieces go to the
-    // workgroups whose full rounds cost least (live row blocks summed over
-    // their tiles; ties by position): every workgroup computes all G costs and
-    // its own rank the same way.  A piece streams its tile's copies but only
-    // the waves of its columns multiply and store, so a leftover tile no
-    // longer keeps one workgroup busy for a whole tile after the rest are
-    // done.  A fuller last round keeps the plain order, whose adjacent tiles
-    // share L2 data.
-    __shared__ int s_cost[kMaxWorkgroups];
-    __shared__ int s_extra, s_piece;
+    // Round k of workgroup w takes tile k G + w.  When tiles differ in cost
+    // (!TRIM), odd rounds run the other way (k G + G - 1 - w): with the tiles
+    // numbered largest class first, this deals them like a longest-first
+    // schedule, and each workgroup's sum comes out nearly equal.  Dealt in
+    // plain order, an XCD's 32 workgroups took 32 consecutive tiles of one
+    // expert every round, and some XCDs finished 15% after others.
+    auto pos = [&](int k, int w) { return k * G + ((!TRIM && (k & 1)) ? G - 1 - w : w); };
+
+    // When the last round is sparse (L <= G / WAVES_N tiles), each of its tiles is
+    // cut into WAVES_N column pieces (one wave column each).  A piece streams
+    // its tile's copies but only the waves of its columns multiply and store,
+    // so a leftover tile no longer keeps one workgroup busy for a whole tile
+    // after the rest are done.  The pieces of leftover tile j go to WAVES_N
+    // workgroups of one XCD (XCD j % 8), which then share the tile's data in
+    // their L2 (pieces of one tile spread over several XCDs each fetched the
+    // tile from HBM and took longer than the whole tile).  The snake order has
+    // already evened out the full rounds.  A fuller last round keeps the plain
+    // order, whose adjacent tiles share L2 data.
     const int F = total / G, L = total - F * G;
-    const bool ranked = !TRIM && L > 0 && WAVES_N * L <= G;
+    const int groups = 8 * (act_xcd / WAVES_N);  // whole groups of WAVES_N slots
+    const bool ranked = !TRIM && L > 0 && L <= groups;
+    int extra = pos(F, vid) < total ? pos(F, vid) : -1, piece = 0;
     if (ranked) {
-        for (int w = tid; w < G; w += NW * kWave) {
-            int c = 0;
-            for (int k = 0; k < F; ++k) {
-                const TileRows tr =
-                    tile_rows<BM, BM / WAVES_M>(w + k * G, p.E, s_tile_start, s_row_off, s_rows);
-                c += (tr.rows + WM - 1) / WM;
-            }
-            s_cost[w] = c;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            const int mine = s_cost[vid];
-            int rank = 0;
-            for (int w = 0; w < G; ++w) rank += s_cost[w] < mine || (s_cost[w] == mine && w < vid);
-            s_extra = rank < WAVES_N * L ? F * G + rank / WAVES_N : -1;
-            s_piece = rank % WAVES_N;
-        }
-        __syncthreads();
+        const int xcd = vid / act_xcd, slot = vid % act_xcd;
+        const int j = (slot / WAVES_N) * 8 + xcd;  // leftover tile of this group
+        extra = j < L ? F * G + j : -1;
+        piece = slot % WAVES_N;
     }
-    const int extra = ranked ? s_extra : (vid < L ? F * G + vid : -1);
-    const int piece = ranked ? s_piece : 0;
 
     int parity = 0;
     for (int k = 0;; ++k, parity ^= 1) {
-        const int t = k < F ? vid + k * G : (k == F ? extra : -1);
+        const int t = k < F ? pos(k, vid) : (k == F ? extra : -1);
         if (t < 0) break;
-        const TileRows tr = tile_rows<BM, BM / WAVES_M>(t, p.E, s_tile_start, s_row_off, s_rows);
+        const TileRows tr = tile_rows<BM, BM / WAVES_M>(t, p.E, s_pre, s_row_off, s_rows);
         const int e = tr.e;
         const int row0 = tr.row0;
         const int rows = tr.rows;
