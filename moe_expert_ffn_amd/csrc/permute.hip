@@ -244,8 +244,9 @@ __global__ __launch_bounds__(256) void quant_scatter_kernel(
 // before r -- the same stable expert-major order as the two-pass sort.  It
 // then quantises its token once and writes the row to its routes' rows.
 // Workgroup 0 also writes the counts, the inclusive prefix, the dropped-route
-// word and the -1 tail of sorted_route.  The x row is requested first, so its
-// load overlaps the histogram.
+// word and the -1 tail of sorted_route.  The x row and the first 2048 expert
+// ids are requested before anything else, and the token-major row is
+// quantised and stored before the sort's prefix, so those latencies overlap.
 constexpr int kFusedMaxR = 8192;
 constexpr int kFusedMaxTopK = 16;
 
@@ -268,7 +269,8 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     const int nchunk = K >> 4;
     const int r_own = t * top_k;
 
-    // the token's row, requested before anything else
+    // Every first load is issued up front: the token's row, the first 2048
+    // expert ids (all of them up to R = 2048) and the token's own ids.
     const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)t * K);
     uint4 raw[MAXC][2];
 #pragma unroll
@@ -279,27 +281,83 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
             raw[i][1] = xr[2 * c + 1];
         }
     }
-
+    int key0[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) key0[u] = route_key(expert_idx, u * 256 + tid, R, E);
+    if (tid < top_k) s_key[tid] = route_key(expert_idx, r_own + tid, R, E);
     for (int e = tid; e <= E; e += 256) {
         h_all[e] = 0;
         h_pre[e] = 0;
     }
-    if (tid < top_k) s_key[tid] = route_key(expert_idx, r_own + tid, R, E);
-    __syncthreads();
+
+    // the row's absolute maximum
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c < nchunk) {
+            const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] & 0xffffu))));
+                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] >> 16))));
+            }
+        }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) s_red[tid >> 6] = amax;
+    __syncthreads();  // counters zeroed; s_key and s_red written
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float scale = amax / 127.0f;
+
+    // histograms: every route's expert, and the routes before this token's
+    // (key E, a dropped route, is counted too, in slot E)
     for (int r0 = 0; r0 < R; r0 += 8 * 256) {
         int key[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) key[u] = route_key(expert_idx, r0 + u * 256 + tid, R, E);
+        for (int u = 0; u < 8; ++u)
+            key[u] = r0 == 0 ? key0[u] : route_key(expert_idx, r0 + u * 256 + tid, R, E);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int r = r0 + u * 256 + tid;
-            if (r < R) {  // key E (dropped) is counted too, in slot E
+            if (r < R) {
                 atomicAdd(&h_all[key[u]], 1);
                 if (r < r_own) atomicAdd(&h_pre[key[u]], 1);
             }
         }
     }
-    __syncthreads();
+
+    // per-token dynamic quantisation; it does not depend on the sort, so the
+    // token-major row is stored while the histograms complete
+    uint4 q[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = tid + i * 256;
+        if (c >= nchunk) continue;
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
+        uint32_t packed[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int idx = j * 4 + h;
+                const uint16_t bits = (uint16_t)((w[idx >> 1] >> ((idx & 1) * 16)) & 0xffffu);
+                int qv = 0;
+                if (amax != 0.0f) {
+                    float r = roundf(h2f(bits) / scale);  // CAST_ROUND: half away from zero
+                    r = fminf(fmaxf(r, -127.0f), 127.0f);
+                    qv = (int)r;
+                }
+                word |= ((uint32_t)qv & 0xffu) << (8 * h);
+            }
+            packed[j] = word;
+        }
+        q[i] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        if (token_major) *reinterpret_cast<uint4 *>(gmA + (size_t)t * K + (size_t)c * 16) = q[i];
+    }
+    __syncthreads();  // histograms complete
+
     if (tid < kWave) {  // exclusive prefix of the counts over experts, four per lane
         int v[4];
         int sum = 0;
@@ -336,67 +394,28 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
         }
         s_dst[tid] = dst;
         expanded_row_idx[r_own + tid] = dst;
-        if (dst >= 0) sorted_route[dst] = r_own + tid;
+        if (dst >= 0) {
+            sorted_route[dst] = r_own + tid;
+            pts1[dst] = scale;
+        }
     }
     if (t == 0) {
         const int valid_rows = s_valid;
         if (tid == 0) err_word[0] = R - valid_rows;
         for (int d = valid_rows + tid; d < R; d += 256) sorted_route[d] = -1;
     }
-
-    // per-token dynamic quantisation, written to every route's row
-    float amax = 0.0f;
+    if (!token_major) {  // the row goes to every route's row
+        __syncthreads();  // publishes s_dst
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
-        if (c < nchunk) {
-            const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] & 0xffffu))));
-                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] >> 16))));
-            }
-        }
-    }
-    amax = wave_max(amax);
-    if (lane == 0) s_red[tid >> 6] = amax;
-    __syncthreads();  // also publishes s_dst
-    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    const float scale = amax / 127.0f;
-#pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
-        if (c >= nchunk) continue;
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
-        uint32_t packed[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int idx = j * 4 + h;
-                const uint16_t bits = (uint16_t)((w[idx >> 1] >> ((idx & 1) * 16)) & 0xffffu);
-                int q = 0;
-                if (amax != 0.0f) {
-                    float r = roundf(h2f(bits) / scale);  // CAST_ROUND: half away from zero
-                    r = fminf(fmaxf(r, -127.0f), 127.0f);
-                    q = (int)r;
-                }
-                word |= ((uint32_t)q & 0xffu) << (8 * h);
-            }
-            packed[j] = word;
-        }
-        const uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        if (token_major) {
-            *reinterpret_cast<uint4 *>(gmA + (size_t)t * K + (size_t)c * 16) = out;
-        } else {
+        for (int i = 0; i < MAXC; ++i) {
+            const int c = tid + i * 256;
+            if (c >= nchunk) continue;
             for (int s2 = 0; s2 < top_k; ++s2) {
                 const int d = s_dst[s2];
-                if (d >= 0) *reinterpret_cast<uint4 *>(gmA + (size_t)d * K + (size_t)c * 16) = out;
+                if (d >= 0) *reinterpret_cast<uint4 *>(gmA + (size_t)d * K + (size_t)c * 16) = q[i];
             }
         }
     }
-    if (tid < top_k && s_dst[tid] >= 0) pts1[s_dst[tid]] = scale;
 }
 
 bool permute_fused_ok(int R, int top_k) { return R <= kFusedMaxR && top_k <= kFusedMaxTopK; }
