@@ -160,6 +160,61 @@ def test_leftover_tiles_split_by_columns():
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
 
 
+@pytest.mark.parametrize("top_k", [1, 17], ids=["one_launch_permute", "two_pass_sort"])
+def test_quantiser_every_fp16_value(top_k):
+    """Rows that hold every finite fp16 value up to the row's maximum (both
+    signs), for twelve row maxima from the smallest subnormal to 65504: each
+    int8 code and scale of the GPU quantiser equals the oracle's (C roundf of
+    the IEEE quotient).  top_k 1 takes the one-launch permute, top_k 17 the
+    two-pass sort and its quantise kernel; both the token-major rows of the
+    forward and the page's scattered rows are checked."""
+    K, E = 32768, 32
+    finite = np.arange(0x7C00, dtype=np.uint16)  # +0 .. 65504
+    maxima = [0x0001, 0x0200, 0x03FF, 0x0400, 0x1800, 0x2E66, 0x3C00, 0x3C01, 0x57F0, 0x5BF0,
+              0x7000, 0x7BFF]
+    rows = []
+    for a in maxima:
+        vals = finite[finite <= a]
+        xs = np.concatenate([vals, vals | 0x8000])
+        for c0 in range(0, len(xs), K - 1):
+            row = np.zeros(K, np.uint16)
+            row[0] = a  # the row's largest magnitude
+            chunk = xs[c0:c0 + K - 1]
+            row[1:1 + len(chunk)] = chunk
+            rows.append(row)
+    M = len(rows)
+    x = np.stack(rows).view(np.float16)
+    rng = np.random.default_rng(6)
+    eidx = np.stack([rng.permutation(E)[:top_k] for _ in range(M)]).astype(np.int32)
+    print(f"[parity] quantiser rows M={M} K={K} top_k={top_k}", flush=True)
+    d = MM.dims(M, K, E, top_k, 128)
+    R = M * top_k
+    cu = dict(device="cuda")
+    xd = torch.from_numpy(x).cuda()
+    ed = torch.from_numpy(eidx).cuda()
+    ws = torch.empty(MM.megamoe_permute_workspace_bytes(d), dtype=torch.uint8, **cu)
+    o = {k: torch.empty(R, dtype=torch.int32, **cu) for k in ("eri", "srt")}
+    cnt = torch.empty(E, dtype=torch.int32, **cu)
+    cum = torch.empty(E, dtype=torch.int32, **cu)
+    qx = torch.empty((M, K), dtype=torch.int8, **cu)
+    pts1 = torch.empty(R, dtype=torch.float32, **cu)
+    MM.megamoe_permute_tokens(d, xd, ed, qx, pts1, o["eri"], o["srt"], cnt, cum, ws)
+    gmA = torch.empty((R, K), dtype=torch.int8, **cu)
+    pts1b = torch.empty(R, dtype=torch.float32, **cu)
+    MM.megamoe_permute(d, xd, ed, gmA, pts1b, o["eri"], o["srt"], cnt, cum, ws)
+    torch.cuda.synchronize()
+    qx_h, gmA_h = qx.cpu().numpy(), gmA.cpu().numpy()
+    eri = o["eri"].cpu().numpy().reshape(M, top_k)
+    p1, p1b = pts1.cpu().numpy(), pts1b.cpu().numpy()
+    for t in range(M):
+        q_ref, s_ref = O.quant_token(x[t])
+        assert np.array_equal(qx_h[t], q_ref), f"token-major row {t} (max {maxima})"
+        for s_ in range(top_k):
+            r = int(eri[t, s_])
+            assert np.array_equal(gmA_h[r], q_ref), f"scattered row of token {t}"
+            assert p1[r] == s_ref and p1b[r] == s_ref, f"scale of token {t}"
+
+
 def test_dropped_routes_error_word():
     w = W.custom(40, 256, 8, 3, 128, name="dropped")
     inp = W.generate(w, seed=2)
