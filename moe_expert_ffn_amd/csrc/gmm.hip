@@ -8,22 +8,27 @@
 // round-robin; the same idea runs on the device here, from the per-expert
 // inclusive row counts, without a host round trip:
 //
-//  * every workgroup rebuilds the per-expert tile prefix in LDS from
-//    expert_cumsum (E <= 256 values, one wave scan), so empty experts
+//  * every workgroup rebuilds the tile numbering in LDS from expert_cumsum
+//    (E <= 256 values, one wave scan per cost class), so empty experts
 //    contribute no tiles and nothing is read back to the host;
-//  * the grid is persistent (CUs x occupancy workgroups) and walks the
-//    flattened tile list; tiles of one expert are ordered n-block-major with
-//    the m-blocks innermost, so the workgroups sharing a weight block are
-//    adjacent in the list;
-//  * the blockIdx -> list position map is XCD-aware: the hardware deals
+//  * an expert's rows are split evenly over its m-blocks, and a tile's cost
+//    class is its number of live 64-row blocks; tiles are numbered largest
+//    class first, then by expert, n-block and m-block, so the m-blocks that
+//    share a weight block are adjacent;
+//  * the grid is persistent (CUs x occupancy workgroups) and deals the tiles
+//    in rounds of one tile per workgroup, backward in odd rounds when costs
+//    differ (a snake, close to a longest-first schedule); a sparse last round
+//    is cut into column pieces;
+//  * the blockIdx -> position map is XCD-aware: the hardware deals
 //    workgroups round-robin over the 8 XCDs, so positions are assigned so that
-//    each XCD works on a contiguous run of the list and its own L2 sees the
+//    each XCD works on a contiguous run of tiles and its own L2 sees the
 //    weight and activation blocks that run shares (the page's 9-column
 //    swizzle serves the same purpose on its hardware).
 //
 // Tiles are fed to v_mfma_i32_16x16x64_i8 from LDS: 64-byte K slices of A rows
 // and packed weight rows are copied global -> LDS by DMA into a ring of
 // stages, fragments are double-buffered in registers.
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -32,7 +37,7 @@
 namespace megamoe {
 
 constexpr int kMaxE = 256;
-constexpr int kMaxWorkgroups = 1024;  // GEMM grid bound (cost table of the last round)
+constexpr int kMaxWorkgroups = 1024;  // GEMM grid bound (4 workgroups per CU at most)
 constexpr int kBK64 = 64;  // K bytes per MFMA step (one 64-byte slice per row)
 constexpr int kPackRows = 256;                 // weight rows per packed n-block (= BN)
 constexpr int kPackBlock = kPackRows * kBK64;  // bytes of one packed (n-block, K slice)
@@ -515,7 +520,7 @@ struct GmmVariant {
     int bm, bn;
     void (*kernel)(GmmParams);
     int threads;
-    int occupancy;  // resident workgroups per CU, filled at first use
+    std::atomic<int> occupancy;  // resident workgroups per CU, filled at first use
 };
 
 static GmmVariant g_variants[] = {
@@ -533,17 +538,18 @@ int gmm_pick_variant(int R, int E) {
 hipError_t launch_gmm(int variant, const GmmParams &prm, int R, int cu_count,
                       hipStream_t stream) {
     GmmVariant &v = g_variants[variant];
-    if (v.occupancy == 0) {
-        int occ = 0;
+    int occ = v.occupancy.load(std::memory_order_relaxed);
+    if (occ == 0) {  // concurrent first calls store the same value
         hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &occ, reinterpret_cast<const void *>(v.kernel), v.threads, 0);
         if (err != hipSuccess) return err;
-        v.occupancy = occ > 0 ? occ : 1;
+        occ = occ > 0 ? occ : 1;
+        v.occupancy.store(occ, std::memory_order_relaxed);
     }
     // Upper bound on the tile count: sum_e ceil(rows_e / BM) <= R / BM + E.
     const int NB = (prm.N + v.bn - 1) / v.bn;
     const long long ub = ((long long)R / v.bm + prm.E) * NB;
-    long long g = (long long)cu_count * v.occupancy;
+    long long g = (long long)cu_count * occ;
     if (ub < g) g = ub;
     g = (g + 7) / 8 * 8;
     if (g < 8) g = 8;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/megamoe.h"
 #include "kernels.hpp"
 
@@ -25,18 +27,22 @@ size_t align_big(size_t v) { return (v + kBigAlign - 1) / kBigAlign * kBigAlign;
 
 bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
+// CU count of the current device, queried once per device.  It only sizes the
+// persistent GEMM grid, so a failed query falls back to MI355X's 256.  The
+// cache is filled with relaxed atomics: concurrent first calls store the same
+// value.
 int cu_count_current() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 struct Layout {
