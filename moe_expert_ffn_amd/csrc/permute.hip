@@ -100,14 +100,23 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
         s_base[e] = 0;
     }
     __syncthreads();
-    // all (block, expert) entries of the table, coalesced; integer sums are
-    // order-free, so LDS atomics accumulate them
-    for (int i = tid; i < B * E; i += kSortBlock) {
-        const int bb = i / E, e = i - bb * E;
-        const int v = block_counts[i];
-        if (v) {
-            atomicAdd(&s_tot[e], v);
-            if (bb < b) atomicAdd(&s_base[e], v);
+    // the table's column sums (all blocks, and the blocks before this one):
+    // thread (part, e) sums expert e over blocks part, part + parts, ... with
+    // coalesced loads, and the partial sums meet in LDS (integer sums are
+    // order-free)
+    {
+        const int parts = kSortBlock / E;  // >= 1 since E <= kMaxExperts = kSortBlock
+        const int e = tid % E, part = tid / E;
+        if (part < parts) {
+            int tot = 0, pre = 0;
+#pragma unroll 8
+            for (int bb = part; bb < B; bb += parts) {
+                const int v = block_counts[(size_t)bb * E + e];
+                tot += v;
+                pre += bb < b ? v : 0;
+            }
+            if (tot) atomicAdd(&s_tot[e], tot);
+            if (pre) atomicAdd(&s_base[e], pre);
         }
     }
     __syncthreads();
