@@ -48,6 +48,10 @@ SMALL = [
     W.custom(1, 128, 4, 2, 128, name="single_token"),
     W.custom(96, 640, 64, 6, 256, routing="zipf", name="skew_E64"),
     W.custom(6000, 128, 64, 6, 128, routing="zipf", name="two_sort_segments"),  # R > 32768
+    W.custom(37, 256, 1, 1, 128, name="single_expert"),             # E = 1: identity sort
+    W.custom(48, 256, 6, 6, 128, name="topk_equals_E"),             # every token to every expert
+    W.custom(64, 32768, 2, 2, 128, name="max_K"),                   # largest supported K
+    W.custom(24, 128, 4, 2, 16384, name="max_I"),                   # largest supported I
 ]
 
 
@@ -234,6 +238,25 @@ def test_dropped_routes_error_word():
     dev2 = H.to_dev(inp2)
     out, dropped = H.run_forward(w, dev2, w1p, w2p)
     assert dropped == 0
+
+
+def test_all_routes_dropped():
+    """Every expert id out of range: no valid row anywhere, the GEMMs have no
+    tiles, the error word counts all R routes and out is exactly zero."""
+    w = W.custom(20, 256, 4, 2, 128, name="all_dropped")
+    inp = W.generate(w, seed=7)
+    inp["expert_idx"][:] = -1
+    o_ref = O.forward(inp)
+    assert o_ref["dropped"] == w.R
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    assert g["dropped"] == w.R
+    _compare_full(w, inp, o_ref, g)
+    out, dropped = H.run_forward(w, dev, w1p, w2p)
+    assert dropped == w.R
+    assert not H.bf16_bits(out).any(), "out must be exactly zero"
 
 
 def test_repeat_launch_bit_identical():
