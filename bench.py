@@ -54,6 +54,9 @@ def parse():
                     help="summarise a rocprofv3 kernel-trace directory into profiles/ and exit")
     ap.add_argument("--pmc-fetch", default=None, help="rocprofv3 FETCH_SIZE output directory")
     ap.add_argument("--pmc-write", default=None, help="rocprofv3 WRITE_SIZE output directory")
+    ap.add_argument("--pmc-mfma", default=None,
+                    help="rocprofv3 output directory of GRBM_GUI_ACTIVE SQ_BUSY_CYCLES "
+                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVES")
     ap.add_argument("--command", default="", help="profiling command line recorded in the summary")
     return ap.parse_args()
 
@@ -152,12 +155,18 @@ def _find(d, suffix):
 def _label_dispatches(rows):
     """Stage label per GEMM dispatch: the GEMM launch that follows the permute
     stage's last kernel is GMM1, the one after SwiGLU is GMM2."""
-    out, last, seen_copy = [], None, set()
+    # one row per dispatch in a trace, one per (dispatch, counter) in a counter
+    # run: the stage of a dispatch follows from the kernel of the dispatch
+    # before it
+    out, seen_copy = [], set()
+    prev_name, cur_id, cur_name = None, None, None
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         name = r["Kernel_Name"].split("(")[0].split("<")[0].replace("void ", "").strip()
         name = name.split("::")[-1]
+        if r["Dispatch_Id"] != cur_id:
+            prev_name, cur_id, cur_name = cur_name, r["Dispatch_Id"], name
         if name.startswith("gmm_i8"):
-            stage = "gmm1" if last in PERMUTE_LAST else "gmm2"
+            stage = "gmm1" if prev_name in PERMUTE_LAST else "gmm2"
         elif name in STAGE_OF_KERNEL:
             stage = STAGE_OF_KERNEL[name]
         elif "copyBuffer" in name and (not seen_copy or r["Dispatch_Id"] in seen_copy):
@@ -167,7 +176,6 @@ def _label_dispatches(rows):
         else:
             stage = name
         out.append((r, name, stage))
-        last = name
     return out
 
 
@@ -224,6 +232,29 @@ def summarize_profile(a):
             wb = write[st] * 1024 * w_scale
             traffic[st] = fb + wb
             lines.append(f"| {st} | {fb/1e6:.1f} | {wb/1e6:.1f} | {(fb+wb)/1e6:.1f} |")
+    if a.pmc_mfma:
+        # MFMA busy cycles are counted per SIMD (256 CUs x 4 SIMDs); the GPU
+        # busy cycles per XCD (8 XCDs), so utilisation = busy / (SIMDs x
+        # per-XCD active cycles)
+        rows = _csv_rows(_find(a.pmc_mfma, "counter_collection.csv"))
+        acc = {}
+        for r, name, stage in _label_dispatches(rows):
+            if stage not in ("gmm1", "gmm2"):
+                continue
+            d = acc.setdefault(stage, {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        lines += ["", "## MFMA utilisation of the GEMMs (rocprofv3 --pmc, summed over the run)", "",
+                  "Utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs).",
+                  "", "| stage | GRBM_GUI_ACTIVE | SQ_VALU_MFMA_BUSY_CYCLES | SQ_BUSY_CYCLES | "
+                  "MFMA busy per SIMD |", "|---|---|---|---|---|"]
+        for st in ("gmm1", "gmm2"):
+            d = acc.get(st)
+            if not d or not d.get("GRBM_GUI_ACTIVE"):
+                continue
+            util = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024.0 * d["GRBM_GUI_ACTIVE"] / 8.0)
+            lines.append(f"| {st} | {d['GRBM_GUI_ACTIVE']:.4g} | "
+                         f"{d.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0):.4g} | "
+                         f"{d.get('SQ_BUSY_CYCLES', 0.0):.4g} | {util:.1%} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     md = os.path.join(ROOT, "profiles", f"pipeline_{w.name}.md")
     with open(md, "w") as f:
