@@ -215,9 +215,9 @@ __device__ __forceinline__ void dma4(const void *gptr, uint32_t lds_base) {
 // Copies are issued for real stages only; over the last NS-2 stages of a tile,
 // where fewer younger copies exist, the wait is for all of them.
 //
-// Weights are read from the tile-contiguous packed layout (see the pack
+// Weights are read from the K-slice-major packed layout (see the pack
 // kernel): one stage of a tile's weight rows is a single contiguous 16 KB
-// block, so each tile streams its weights sequentially.
+// block, and the blocks of all tiles for one K slice are adjacent.
 //
 // The tile's per-channel scales are copied to one of two LDS slots (by tile
 // parity) when the tile starts, ahead of its stage copies in issue order, so
@@ -371,8 +371,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         // l & 3), taking the chunk that the swizzle puts there.  A rows past
         // the group's end repeat its last row (their results are not stored).
         const int8_t *src[LPW];
-        const int8_t *btile =
-            p.B + ((size_t)e * NB + nblk) * (size_t)nst * kPackBlock;
+        // packed weights are K-slice-major: the block of (expert e, n-block
+        // nblk) for K slice ks sits at ((ks * E + e) * NB + nblk) blocks
+        const int8_t *btile = p.B + ((size_t)e * NB + nblk) * kPackBlock;
+        const size_t bstep = (size_t)p.E * NB * kPackBlock;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int pch = (wave + j * NW) * 64 + lane;
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
-                const size_t step = j < kAJ ? (size_t)kBK64 : (size_t)kPackBlock;
+                const size_t step = j < kAJ ? (size_t)kBK64 : bstep;
                 dma16(src[j] + (size_t)stage * step,
                       __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024)));
             }
@@ -469,14 +471,18 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     }
 }
 
-// Weight pack: logical [E][Kred][N] -> tile-contiguous [E][NB][Kred/64][256][64]
-// (NB = ceil(N / 256)): for n-block nb and K slice ks, the 256 weight rows
-// n = 256 nb + r hold bytes w[e][64 ks + kb][n], kb = 0..63, in one
-// contiguous 16 KB block; rows n >= N are zero.  One 64 x 64 (k, n) tile per
+// Weight pack: logical [E][Kred][N] -> K-slice-major [Kred/64][E][NB][256][64]
+// (NB = ceil(N / 256)): for K slice ks, expert e and n-block nb, the 256
+// weight rows n = 256 nb + r hold bytes w[e][64 ks + kb][n], kb = 0..63, in
+// one contiguous 16 KB block; rows n >= N are zero.  When the GEMM streams
+// weights (few rows per expert), all tiles advance through K together, so at
+// any moment the grid reads one window of adjacent blocks; that was measured
+// 3-5% faster at decode than keeping each tile's K slices together, and
+// within 1.5% either way at the larger shapes.  One 64 x 64 (k, n) tile per
 // workgroup, transposed through LDS; its output is 64 rows of one block.
 __global__ __launch_bounds__(256) void pack_tiles_kernel(const int8_t *__restrict__ w,
                                                          int8_t *__restrict__ wp, int Kred,
-                                                         int N, int NB) {
+                                                         int N, int NB, int E) {
     __shared__ int8_t tile[64][65];
     const int e = blockIdx.z;
     const int ks = blockIdx.y, n0 = blockIdx.x * 64;
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(256) void pack_tiles_kernel(const int8_t *__restric
     }
     __syncthreads();
     const int nb = n0 / kPackRows, r0 = n0 % kPackRows;
-    int8_t *dst = wp + (((size_t)e * NB + nb) * (Kred / kBK64) + ks) * kPackBlock;
+    int8_t *dst = wp + (((size_t)ks * E + e) * NB + nb) * kPackBlock;
     for (int r = ty; r < 64; r += 4) dst[(size_t)(r0 + r) * kBK64 + tx] = tile[tx][r];
 }
 
@@ -501,7 +507,7 @@ size_t packed_weight_bytes(int E, int Kred, int N) {
 hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipStream_t stream) {
     const int NB = (N + kPackRows - 1) / kPackRows;
     dim3 grid(NB * kPackRows / 64, Kred / kBK64, E), block(256);
-    hipLaunchKernelGGL(pack_tiles_kernel, grid, block, 0, stream, w, wp, Kred, N, NB);
+    hipLaunchKernelGGL(pack_tiles_kernel, grid, block, 0, stream, w, wp, Kred, N, NB, E);
     return hipGetLastError();
 }
 

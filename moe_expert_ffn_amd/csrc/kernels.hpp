@@ -45,7 +45,7 @@ hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,
 hipError_t launch_unpermute(const uint16_t *gmm2_out, const float *pts2,
                             const int32_t *expanded_row_idx, const float *probs, int M, int K,
                             int top_k, uint16_t *out, hipStream_t stream);
-// Weight pack into the GEMM's tile-contiguous layout; packed_weight_bytes is
+// Weight pack into the GEMM's K-slice-major layout; packed_weight_bytes is
 // its size for E experts of a logical [Kred][N] weight.
 size_t packed_weight_bytes(int E, int Kred, int N);
 hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipStream_t stream);
