@@ -9,7 +9,8 @@ gmC and gmm2_out (fp16 of an exact int32 times an fp32 scale) are expected to
 match bit for bit wherever the inputs match; that is checked too.
 
 Small shapes run the whole oracle and compare every element; they cover each
-GEMM tile variant (mean rows per expert <= 40, <= 96, <= 192, more), ragged
+GEMM tile configuration (64-row tiles with short and long K loops,
+256-row tiles), ragged
 N tails, empty experts, M = 1, a single hot expert and dropped routes.  The
 full workload sizes compare the sort and quantisation everywhere and the GEMM
 chain on sampled tokens the oracle evaluates one at a time.
@@ -44,6 +45,7 @@ SMALL = [
     W.custom(700, 256, 4, 2, 384, name="v3_mean350"),               # 256x256 tiles, ragged
     W.custom(300, 4096, 5, 2, 256, name="v4_mean120_longK"),        # 256x256, dead row blocks, long K
     W.custom(256, 512, 64, 8, 2048, name="v5_two_tiles_per_wg"),    # 64-row tiles, 2 per workgroup
+    W.custom(200, 4096, 8, 2, 256, name="v6_stream_longK"),         # 64-row tiles, long K loop
     W.custom(512, 256, 16, 4, 128, routing="zipf_empty", name="zipf_empty_groups"),
     W.custom(1, 128, 4, 2, 128, name="single_token"),
     W.custom(96, 640, 64, 6, 256, routing="zipf", name="skew_E64"),
