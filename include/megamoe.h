@@ -5,9 +5,8 @@
  * page (pto-isa, kernels/manual/a2a3/dispatch_mega_combine), stage overview
  * and sections 1-7: FrontReorder -> (Dispatch) -> GMM1 -> SwiGLU -> GMM2 ->
  * (Combine) -> Unpermute.  With a single rank, Dispatch is the identity (the
- * quantised rows are written straight into the expert-major A matrix) and
- * Combine's remote store becomes the dequant-and-cast that Unpermute applies
- * in registers.
+ * quantised rows go straight into the A operand of GMM1) and Combine's remote
+ * store becomes the dequant-and-cast that Unpermute applies in registers.
  *
  * Conventions shared by every entry point
  *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
@@ -146,7 +145,11 @@ int megamoe_gmm1_gather(const megamoe_dims *d, const int8_t *qx, const int32_t *
 /* Stage 4 SwiGLU, section 4: per valid row,
  *   c = fp32(gmC) * pts1;  y = silu(c[0:I]) * c[I:2I];  pts2 = max|y| / 127;
  *   q2 = rint(y * (127 / max|y|))  (int8)
- * Valid rows are [0, expert_cumsum[E-1]).  q2 int8 [R, I], pts2 fp32 [R]. */
+ * Valid rows are [0, expert_cumsum[E-1]).  q2 int8 [R, I], pts2 fp32 [R].
+ * silu(u) = u / (1 + exp(-u)) is evaluated with the hardware base-2 exponential
+ * and reciprocal plus one correction of the quotient, a few ulp from the IEEE
+ * expression (on the decode, large and skewed workloads every q2 code and
+ * pts2 equals the IEEE result). */
 int megamoe_swiglu_quant(const megamoe_dims *d, const uint16_t *gmC, const float *pts1,
                          const int32_t *expert_cumsum, int8_t *q2, float *pts2, void *stream);
 
