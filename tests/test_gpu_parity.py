@@ -11,7 +11,8 @@ match bit for bit wherever the inputs match; that is checked too.
 Small shapes run the whole oracle and compare every element; they cover each
 GEMM tile configuration (64-row tiles with short and long K loops,
 256-row tiles), ragged
-N tails, empty experts, M = 1, a single hot expert and dropped routes.  The
+N tails, empty experts, M = 1, a single hot expert and dropped routes; 32
+seeded random shapes add combinations no hand-picked case covers.  The
 full workload sizes compare the sort and quantisation everywhere and the GEMM
 chain on sampled tokens the oracle evaluates one at a time.
 """
@@ -240,6 +241,56 @@ def test_dropped_routes_error_word():
     dev2 = H.to_dev(inp2)
     out, dropped = H.run_forward(w, dev2, w1p, w2p)
     assert dropped == 0
+
+
+def _random_cases(n: int = 32, seed: int = 2024):
+    """Seeded random shapes within the supported bounds, each small enough for
+    the whole oracle (R K I <= 2^30): M, E, top_k, K, I and the routing drawn
+    independently; about a third drop some routes (expert ids -1, E, E + 7)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        E = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16, 31, 32, 48, 64, 100]))
+        top_k = int(rng.integers(1, min(E, 12) + 1))
+        M = int(rng.integers(1, 700))
+        K = 128 * int(rng.integers(1, 33))
+        I = 128 * int(rng.integers(1, 17))
+        routing = str(rng.choice(["uniform", "zipf", "zipf_empty"]))
+        if routing == "zipf_empty" and top_k > (3 * E) // 4:
+            routing = "zipf"
+        if M * top_k * K * I > 1 << 30:
+            continue
+        drop = float(rng.choice([0.0, 0.0, 0.03]))
+        cases.append((len(cases), M, K, E, top_k, I, routing, drop))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(),
+                         ids=lambda c: f"r{c[0]:02d}_M{c[1]}_K{c[2]}_E{c[3]}_k{c[4]}_I{c[5]}"
+                                       f"_{c[6]}{'_drop' if c[7] else ''}")
+def test_random_shapes(case):
+    """Every intermediate against the full oracle on seeded random shapes,
+    the forward bit-equal to the staged run, and the forward's own first two
+    stages bit-equal to the page's."""
+    idx, M, K, E, top_k, I, routing, drop = case
+    w = W.custom(M, K, E, top_k, I, routing=routing, name=f"random{idx}")
+    print(f"[parity] {w.describe()} drop {drop}", flush=True)
+    inp = W.generate(w, seed=100 + idx)
+    if drop:
+        rng = np.random.default_rng(200 + idx)
+        hit = rng.random(inp["expert_idx"].shape) < drop
+        bad = rng.choice(np.array([-1, E, E + 7], np.int32), size=inp["expert_idx"].shape)
+        inp["expert_idx"] = np.where(hit, bad, inp["expert_idx"]).astype(np.int32)
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    out, dropped = H.run_forward(w, dev, w1p, w2p)
+    assert dropped == o_ref["dropped"]
+    assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
+    _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
 
 
 def test_all_routes_dropped():
