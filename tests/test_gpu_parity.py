@@ -167,6 +167,50 @@ def test_leftover_tiles_split_by_columns():
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
 
 
+def _stream_tiles(R: int, E: int, N: int, counts: np.ndarray, cus: int):
+    """Tile count and launch grid of the 64-row GEMM configuration (two
+    workgroups per CU), as the library computes them."""
+    NB = (N + 255) // 256
+    total = int(sum((int(c) + 63) // 64 for c in counts)) * NB
+    grid = min(2 * cus, (R // 64 + E) * NB)
+    return total, max(8, (grid + 7) // 8 * 8)
+
+
+@pytest.mark.parametrize("shape", ["one_round", "partial_round"])
+def test_trimmed_grid(shape):
+    """Weight-streaming GEMMs (64-row tiles) whose tile count does not fill
+    the launch grid evenly, so the active grid is trimmed.  one_round: GMM1
+    has 256 tiles (16 experts with exactly 64 rows, 16 column blocks) for 512
+    workgroups.  partial_round: both GEMMs have tile counts that leave the
+    last round of the full grid partly filled.  Every element is compared
+    with the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if shape == "one_round":
+        w = W.custom(128, 256, 16, 8, 2048, name="one_round")
+        inp = W.generate(w, seed=11)
+        t = np.arange(w.M)[:, None]
+        inp["expert_idx"] = ((8 * t + np.arange(8)[None, :]) % 16).astype(np.int32)
+    else:
+        w = W.custom(512, 1536, 64, 2, 512, name="partial_round")
+        inp = W.generate(w, seed=12)
+    counts = np.bincount(inp["expert_idx"].ravel(), minlength=w.E)
+    assert (w.R + w.E - 1) // w.E <= 96, "the shape must take the 64-row tiles"
+    for N in (w.N1, w.K):
+        total, grid = _stream_tiles(w.R, w.E, N, counts, cus)
+        print(f"[parity] N {N}: {total} tiles, full grid {grid}", flush=True)
+    print(f"[parity] {w.describe()}", flush=True)
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    out, dropped = H.run_forward(w, dev, w1p, w2p)
+    assert dropped == 0
+    assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
+
+
 @pytest.mark.parametrize("top_k", [1, 17], ids=["one_launch_permute", "two_pass_sort"])
 def test_quantiser_every_fp16_value(top_k):
     """Rows that hold every finite fp16 value up to the row's maximum (both
