@@ -6,7 +6,9 @@
 // token once (scale = max|x| / 127, q = CAST_ROUND(x / scale)) and write that
 // row to every destination row of the token's routes.  Dispatch (section 2) is
 // the identity on one rank, so the rows go straight to the expert-major A
-// matrix of GMM1.
+// matrix of GMM1.  In the forward (token_major) each token's row is written
+// once instead, to a token-major [M, K] matrix, and GMM1 gathers its
+// expert-major rows from it through the sorted route list.
 //
 // The page sorts with merge-sort instructions sized to its 192 KiB buffer.
 // With at most 256 expert keys a counting sort reaches the same stable order
