@@ -18,6 +18,8 @@ chain on sampled tokens the oracle evaluates one at a time.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 
@@ -335,6 +337,37 @@ def test_random_shapes(case):
     assert dropped == o_ref["dropped"]
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+
+
+def _random_cases_wide(n: int = 60, seed: int = 4242):
+    """Wider seeded random shapes: E up to 256, top_k up to 16, M up to 4000,
+    K up to 8192, I up to 4096 (R K I <= 3 * 2^30, a few seconds of oracle
+    each), 5% of routes dropped in a third of them."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        E = int(rng.choice([1, 2, 6, 16, 33, 64, 128, 200, 256]))
+        top_k = int(rng.integers(1, min(E, 16) + 1))
+        M = int(rng.integers(1, 4000))
+        K = 128 * int(rng.integers(1, 65))
+        I = 128 * int(rng.integers(1, 33))
+        routing = str(rng.choice(["uniform", "zipf", "zipf_empty"]))
+        if routing == "zipf_empty" and top_k > (3 * E) // 4:
+            routing = "zipf"
+        if M * top_k * K * I > 3 << 30 or M * top_k * K >= 1 << 31:
+            continue
+        drop = float(rng.choice([0.0, 0.0, 0.05]))
+        cases.append((len(cases), M, K, E, top_k, I, routing, drop))
+    return cases
+
+
+@pytest.mark.skipif(os.environ.get("MEGAMOE_WIDE_SWEEP") != "1",
+                    reason="about a minute of oracle time; set MEGAMOE_WIDE_SWEEP=1")
+@pytest.mark.parametrize("case", _random_cases_wide(),
+                         ids=lambda c: f"w{c[0]:02d}_M{c[1]}_K{c[2]}_E{c[3]}_k{c[4]}_I{c[5]}")
+def test_random_shapes_wide(case):
+    """test_random_shapes on the wider shapes above."""
+    test_random_shapes(case)
 
 
 def test_all_routes_dropped():
