@@ -288,9 +288,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     __shared__ int s_row_off[kMaxE];
     __shared__ int s_rows[kMaxE];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
+    // the wave index is uniform: kept in a scalar register, so that no
+    // vector register holds threadIdx across the K loop
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = __lane_id();
     const int N = p.N, Kred = p.Kred;
     const int NB = (N + BN - 1) / BN;
     const int total = build_schedule<BM, BM / WAVES_M>(p, NB, s_pre, s_row_off, s_rows);
