@@ -85,3 +85,55 @@ def test_null_and_misaligned_pointers_rejected():
 def test_strerror():
     assert MM.strerror(0) == "ok"
     assert "workspace" in MM.strerror(3)
+
+
+# Every device-pointer argument of the compute entry points, by position after
+# the dims pointer; None marks the workspace size (a size_t).  Nullable
+# arguments (the debug accumulators) are listed separately.
+_POINTER_ARGS = {
+    "megamoe_prepack_w1": (2, ()),
+    "megamoe_prepack_w2": (2, ()),
+    "megamoe_forward": (9, ()),               # x .. out, workspace, then its size
+    "megamoe_permute": (9, ()),
+    "megamoe_permute_tokens": (9, ()),
+    "megamoe_gmm1": (6, (5,)),
+    "megamoe_gmm1_gather": (7, (6,)),
+    "megamoe_swiglu_quant": (5, ()),
+    "megamoe_gmm2": (6, (5,)),
+    "megamoe_unpermute": (5, ()),
+}
+
+
+def _no_gpu():
+    try:
+        import torch
+    except ImportError:
+        return True
+    return torch.cuda.device_count() == 0  # counts devices without initialising one
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="passes placeholder device addresses; host-only")
+@pytest.mark.parametrize("name", sorted(_POINTER_ARGS))
+def test_every_pointer_argument_checked(name):
+    """For every required device pointer of every compute entry point, a null
+    or a misaligned value is rejected with MEGAMOE_EINVAL, and a misaligned
+    nullable one too; nothing is launched."""
+    lib = MM.load()
+    fn = getattr(lib, name)
+    n_ptr, nullable = _POINTER_ARGS[name]
+    d = MM.dims(16, 256, 4, 2, 128)
+    good, odd = 0x10000, 0x10004
+    sized = name in ("megamoe_forward", "megamoe_permute", "megamoe_permute_tokens")
+
+    def call(ptrs):
+        args = [ctypes.byref(d)] + [ctypes.c_void_p(v) if v else None for v in ptrs]
+        if sized:
+            args.append(ctypes.c_size_t(1 << 40))
+        args.append(None)  # stream
+        return fn(*args)
+
+    for pos in range(n_ptr):
+        for bad in ((0, odd) if pos not in nullable else (odd,)):
+            ptrs = [good] * n_ptr
+            ptrs[pos] = bad
+            assert call(ptrs) == 1, (name, pos, hex(bad))
