@@ -191,6 +191,16 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
         : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint (streamed data: the weights).
+__device__ __forceinline__ void dma16_nt(const void *gptr, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, off nt"
+        :
+        : "s"(lds_base), "v"(gptr)
+        : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -400,8 +410,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
                 const size_t step = j < kAJ ? (size_t)kBK64 : bstep;
-                dma16(src[j] + (size_t)stage * step,
-                      __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024)));
+                const uint32_t dst =
+                    __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024));
+                // weights that are streamed once (TRIM) carry the non-temporal hint
+                if (TRIM && j >= kAJ) dma16_nt(src[j] + (size_t)stage * step, dst);
+                else dma16(src[j] + (size_t)stage * step, dst);
             }
         };
 
