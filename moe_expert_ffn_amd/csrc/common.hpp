@@ -10,6 +10,17 @@ constexpr int kWave = 64;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+// 16-byte loads and stores with the non-temporal hint, for data that is
+// read or written once per forward (streaming through the caches)
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+    const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+__device__ __forceinline__ void store_nt16(void *p, uint4 v) {
+    __builtin_nontemporal_store(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w},
+                                reinterpret_cast<v4i *>(p));
+}
+
 // fp16 bits -> fp32 (exact).
 __device__ __forceinline__ float h2f(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);

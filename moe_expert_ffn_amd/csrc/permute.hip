@@ -204,8 +204,8 @@ __global__ __launch_bounds__(256) void quant_scatter_kernel(
     for (int i = 0; i < MAXC; ++i) {
         const int c = tid + i * 256;
         if (c < nchunk) {
-            raw[i][0] = xr[2 * c];
-            raw[i][1] = xr[2 * c + 1];
+            raw[i][0] = load_nt16(xr + 2 * c);  // x is read once
+            raw[i][1] = load_nt16(xr + 2 * c + 1);
             const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -298,8 +298,8 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     for (int i = 0; i < MAXC; ++i) {
         const int c = tid + i * 256;
         if (c < nchunk) {
-            raw[i][0] = xr[2 * c];
-            raw[i][1] = xr[2 * c + 1];
+            raw[i][0] = load_nt16(xr + 2 * c);  // x is read once
+            raw[i][1] = load_nt16(xr + 2 * c + 1);
         }
     }
     int key0[8];

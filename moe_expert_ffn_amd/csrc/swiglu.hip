@@ -60,8 +60,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void swiglu_quant_kernel(
     for (int i = 0; i < MAXC; ++i) {
         const int c = lane + i * kWave;
         if (c < nchunk) {
-            uraw[i] = *reinterpret_cast<const uint4 *>(crow + c * 8);
-            graw[i] = *reinterpret_cast<const uint4 *>(crow + I + c * 8);
+            uraw[i] = load_nt16(crow + c * 8);  // gmC is read once
+            graw[i] = load_nt16(crow + I + c * 8);
         }
     }
     const float p1 = pts1[row];

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
         for (int u = 0; u < kSlotBatch; ++u) {
             if (d[u] >= 0) {  // d < 0: dropped route or past top_k
                 sc[u] = pts2[d[u]];
-                raw[u] = *reinterpret_cast<const uint4 *>(gmm2_out + (size_t)d[u] * K + c * 8);
+                // each GMM2 row is read once: non-temporal
+                raw[u] = load_nt16(gmm2_out + (size_t)d[u] * K + c * 8);
             }
         }
 #pragma unroll
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = f2bf_pk(acc[2 * j], acc[2 * j + 1]);
-    *reinterpret_cast<uint4 *>(out + (size_t)t * K + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    store_nt16(out + (size_t)t * K + c * 8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
 hipError_t launch_unpermute(const uint16_t *gmm2_out, const float *pts2,
