@@ -270,7 +270,8 @@ __device__ __forceinline__ void store_tile_lds(const GmmParams &p, const v4i (&a
     }
 }
 
-template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true, int PRIO = 0>
+template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true, int PRIO = 0,
+          bool NTB = TRIM>
 __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
     // PRIO > 0 (two workgroups per CU that stream weights): the older of the
     // two workgroups on a CU wins the CU's arbitration, and with equal work
@@ -412,8 +413,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 const size_t step = j < kAJ ? (size_t)kBK64 : bstep;
                 const uint32_t dst =
                     __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024));
-                // weights that are streamed once (TRIM) carry the non-temporal hint
-                if (TRIM && j >= kAJ) dma16_nt(src[j] + (size_t)stage * step, dst);
+                // weights that are read by one tile only (NTB) carry the non-temporal hint
+                if (NTB && j >= kAJ) dma16_nt(src[j] + (size_t)stage * step, dst);
                 else dma16(src[j] + (size_t)stage * step, dst);
             }
         };
@@ -538,7 +539,14 @@ hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipS
 //    twice the copies in flight, and they alternate priority every 16 K
 //    steps so that neither finishes long after the other;
 //  * more rows: MFMA bound; 256 x 256 tiles on 16 waves (64 x 64 per wave),
-//    which beat 8-wave layouts of the same tile on every shape measured.
+//    which beat 8-wave layouts of the same tile at the large shapes;
+//  * up to 256 rows per expert (one m-block for most experts), the same
+//    tiles with the weight copies marked non-temporal: each weight block is
+//    read once, and keeping it out of the caches left them to the
+//    activations (mid-size shapes 2-6% faster).  With several m-blocks per
+//    expert the hint evicted the weight blocks they share (large 4-7% slower).
+//  The weight-streaming 64-row tiles always carry the hint (decode GMM1
+//  159 -> 139 us, GMM2 90 -> 80 us).
 // ---------------------------------------------------------------------------
 struct GmmVariant {
     int bm, bn;
@@ -550,13 +558,18 @@ struct GmmVariant {
 static GmmVariant g_variants[] = {
     {64, 256, gmm_i8_ring_kernel<64, 1, 4, 3, true, true, 16>, 256, 0},
     {256, 256, gmm_i8_ring_kernel<256, 4, 4, 4, false>, 1024, 0},
+    {256, 256, gmm_i8_ring_kernel<256, 4, 4, 4, false, true, 0, true>, 1024, 0},
 };
 
 int gmm_num_variants() { return (int)(sizeof(g_variants) / sizeof(g_variants[0])); }
 
 int gmm_pick_variant(int R, int E) {
     const int mean = (R + E - 1) / E;
-    return mean <= 96 ? 0 : 1;
+    if (mean <= 96) return 0;
+    // up to 256 rows per expert most weight blocks are read by one tile only,
+    // so their copies carry the non-temporal hint; above that, the m-blocks
+    // of an expert share each weight block through L2
+    return mean <= 256 ? 2 : 1;
 }
 
 hipError_t launch_gmm(int variant, const GmmParams &prm, int R, int cu_count,
