@@ -26,6 +26,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     W.custom(96, 1024, 8, 4, 256, name="graph_fused_permute"),      # R <= 8192: one-launch permute
     W.custom(2500, 256, 16, 4, 128, name="graph_two_pass_sort"),     # R > 8192: two-pass sort
+    W.custom(256, 1024, 8, 4, 256, name="graph_mid_rows"),           # 128 rows per expert
 ]
 
 
