@@ -10,7 +10,7 @@ match bit for bit wherever the inputs match; that is checked too.
 
 Small shapes run the whole oracle and compare every element; they cover each
 GEMM tile configuration (64-row tiles with short and long K loops,
-256-row tiles), ragged
+256-row tiles with and without non-temporal weight copies), ragged
 N tails, empty experts, M = 1, a single hot expert and dropped routes; 32
 seeded random shapes add combinations no hand-picked case covers.  The
 full workload sizes compare the sort and quantisation everywhere and the GEMM
@@ -44,9 +44,9 @@ SMALL = [
     W.WORKLOADS["tiny"],
     W.custom(64, 384, 16, 4, 128, name="v0_mean16_raggedN"),        # 64-row tiles, N=384
     W.custom(200, 256, 6, 2, 256, name="v1_mean67"),                # 64-row tiles
-    W.custom(333, 512, 8, 3, 128, name="v2_mean125"),               # 256x256 tiles
+    W.custom(333, 512, 8, 3, 128, name="v2_mean125"),               # 256x256 tiles, nt weights
     W.custom(700, 256, 4, 2, 384, name="v3_mean350"),               # 256x256 tiles, ragged
-    W.custom(300, 4096, 5, 2, 256, name="v4_mean120_longK"),        # 256x256, dead row blocks, long K
+    W.custom(300, 4096, 5, 2, 256, name="v4_mean120_longK"),        # 256x256 nt, dead row blocks, long K
     W.custom(256, 512, 64, 8, 2048, name="v5_two_tiles_per_wg"),    # 64-row tiles, 2 per workgroup
     W.custom(200, 4096, 8, 2, 256, name="v6_stream_longK"),         # 64-row tiles, long K loop
     W.custom(512, 256, 16, 4, 128, routing="zipf_empty", name="zipf_empty_groups"),
