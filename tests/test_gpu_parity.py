@@ -57,6 +57,8 @@ SMALL = [
     W.custom(48, 256, 6, 6, 128, name="topk_equals_E"),             # every token to every expert
     W.custom(64, 32768, 2, 2, 128, name="max_K"),                   # largest supported K
     W.custom(24, 128, 4, 2, 16384, name="max_I"),                   # largest supported I
+    W.custom(300, 256, 256, 8, 128, name="max_E_one_launch"),      # largest supported E
+    W.custom(1100, 128, 256, 8, 128, routing="zipf", name="max_E_two_pass"),  # R > 8192
 ]
 
 
