@@ -537,7 +537,11 @@ hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipS
 //  * few rows per expert: the GEMM streams weights (HBM bound); a 64-row tile
 //    with a 3-stage ring fits twice per CU, so two workgroups per CU keep
 //    twice the copies in flight, and they alternate priority every 16 K
-//    steps so that neither finishes long after the other;
+//    steps so that neither finishes long after the other.  Once many
+//    experts need a second 64-row block, whose tiles stream the weights
+//    again, the 256-row tiles win: at K = 7168, E = 32, uniform routing, the
+//    64-row tiles were 10% faster at 48 and 52 mean rows and up to 42% slower
+//    from 56 on;
 //  * more rows: MFMA bound; 256 x 256 tiles on 16 waves (64 x 64 per wave),
 //    which beat 8-wave layouts of the same tile at the large shapes;
 //  * up to 256 rows per expert (one m-block for most experts), the same
@@ -565,7 +569,7 @@ int gmm_num_variants() { return (int)(sizeof(g_variants) / sizeof(g_variants[0])
 
 int gmm_pick_variant(int R, int E) {
     const int mean = (R + E - 1) / E;
-    if (mean <= 96) return 0;
+    if (mean <= 52) return 0;
     // up to 256 rows per expert most weight blocks are read by one tile only,
     // so their copies carry the non-temporal hint; above that, the m-blocks
     // of an expert share each weight block through L2
