@@ -3,20 +3,25 @@
 
 One step = one pass of the whole hot path (route sort + quant scatter, GMM1,
 SwiGLU + re-quant, GMM2, combine + unpermute) over one batch of synthetic
-inputs already resident in HBM.  The default workload is the decode-size
-forward (M=128, K=7168, E=32, top-k 8, I=2048).  Prints ONE JSON line.
+inputs already resident in HBM.  The default workload is the largest
+single-GPU forward (M=2048, K=7168, E=32, top-k 8, I=2048), where the grouped
+GEMMs are bound by the int8 matrix cores; --workload picks decode, mid, skewed
+or skewed_empty instead.  Prints ONE JSON line.
 
-Timing.  The headline step is one megamoe_forward call: about 0.2 s of
-untimed calls (the clocks of an idle GPU take that long to settle under load),
-W untimed steps, then K timed steps enqueued back to back between two device
-synchronisations.  The
-per-stage durations (and the roofline of the dominant kernel) come from a
-second timed loop of K steps that calls the stage entry points megamoe_forward
-is made of (megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
+Timing.  The headline step is one megamoe_forward call.  About 0.2 s of
+untimed calls come first (the clocks of an idle GPU take that long to settle
+under load), then W untimed steps, then K timed steps.  Before every timed
+step a 512 MiB device write flushes the L2 caches and the 256 MB memory-side
+cache, so each forward finds its inputs in HBM only; HIP events on the launch
+stream bracket the forward itself, and the K steps are bracketed by device
+synchronisations.  The same K forwards enqueued back to back without the
+flush are reported beside it.  The per-stage durations (and the roofline of
+the dominant kernel) come from a second timed loop of K flushed steps that
+calls the stage entry points megamoe_forward is made of
+(megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
 megamoe_gmm2, megamoe_unpermute) -- the same kernels, in the same order --
-with HIP events recorded on the launch stream between the stages (the event
-records cost a little, so that loop's step time is reported separately).  The forward
-captured into a HIP graph and replayed is timed as well.
+with HIP events recorded on the launch stream between the stages.  The
+forward captured into a HIP graph and replayed is timed as well.
 """
 from __future__ import annotations
 
@@ -35,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + GMM int8 TOPS (% MFMA peak), 1x MI355X"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s (no sparsity)
+FLUSH_BYTES = 512 << 20        # > 2x the 256 MB memory-side cache
 STAGES = ["permute", "gmm1", "swiglu", "gmm2", "unpermute"]
 
 
@@ -43,11 +49,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--workload", default="large")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=None,
-                    help="tokens of the workload the oracle runs for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of each leg of the oracle baseline")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the matrix-core rate probe reported beside the roofline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profile", default=None, metavar="TRACE_DIR",
@@ -99,33 +107,106 @@ def traffic_from_profile(kernel_src: str, workload: str, stage: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, n_tokens: int | None):
+def cpu_baseline(w, inp, budget_s: float):
+    """The C oracle (unchanged, plain loops) timed on this host on a bounded
+    sample of the workload: its per-token forward (quantise, both GEMMs,
+    SwiGLU, combine; every route of the token) over the first tokens, once on
+    one thread and once on a pool of as many threads as this process may use.
+    ctypes releases the interpreter lock inside the C call, so the pool runs
+    the tokens in parallel."""
+    import concurrent.futures as cf
     from oracle import oracle as O
-    M = w.M if n_tokens is None else min(n_tokens, w.M)
-    sub = dict(inp)
-    for k in ("x", "expert_idx", "probs"):
-        sub[k] = np.ascontiguousarray(inp[k][:M])
-    times = []
-    while len(times) < 5 and sum(times) < 10.0:  # about 10 s of CPU work
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    n1 = 0
+    while n1 < w.M and time.perf_counter() - t0 < budget_s:
+        O.forward_token(inp, n1)
+        n1 += 1
+    dt1 = time.perf_counter() - t0
+    # the pool leg: about the same wall time at perfect scaling
+    n2 = min(w.M, max(cores, n1 * cores))
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
         t0 = time.perf_counter()
-        O.forward(sub, E=w.E)
-        times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
-    return {"value": M / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{M} of {w.M} tokens of the {w.name} workload (all their routes, "
-                      f"all stages), single-threaded C oracle, median of {len(times)} runs "
-                      f"of {dt:.1f} s",
+        list(ex.map(lambda t: O.forward_token(inp, t), range(n2)))
+        dt2 = time.perf_counter() - t0
+    return {"value": n2 / dt2, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"tokens 0..{n2 - 1} of the {w.name} workload ({w.M} tokens), each "
+                      f"through the oracle's per-token forward (all its routes, all stages), "
+                      f"on {cores} threads: {dt2:.1f} s",
+            "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"tokens 0..{n1 - 1}, one thread: {dt1:.1f} s"},
             "cpu": _cpu_model()}
 
 
+def mfma_rate_probe(torch, ms_target: float = 100.0) -> dict:
+    """Matrix-core rate with no memory traffic (libmegamoe_probe.so): one
+    1024-thread workgroup per CU issuing back-to-back int8 16x16x64 MFMAs from
+    registers, once with random operands (the GEMMs' data) and once with zero
+    operands; the achieved TOP/s and the shader clock (s_memtime against the
+    100 MHz s_memrealtime) for each.  A context figure for the roofline: the
+    roofline's peak stays the published dense int8 rate."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_expert_ffn_amd", "libmegamoe_probe.so"))
+    P, i32 = ctypes.c_void_p, ctypes.c_int
+    fn = lib.megamoe_probe_mfma_rate
+    fn.argtypes, fn.restype = [P, i32, i32, i32, P, P, P], i32
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_words = 1 << 20
+    ticks = torch.empty(2 * cus, dtype=torch.int64, device="cuda")
+    sink = torch.empty(cus * 1024, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ops_per_iter = cus * 16 * 16 * 32768
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for kind in ("random", "zero"):
+        if kind == "random":
+            opnd = torch.randint(-2**31, 2**31 - 1, (n_words,), dtype=torch.int32, device="cuda",
+                                 generator=g)
+        else:
+            opnd = torch.zeros(n_words, dtype=torch.int32, device="cuda")
+
+        def launch(iters):
+            rc = fn(ctypes.c_void_p(opnd.data_ptr()), n_words, iters, cus,
+                    ctypes.c_void_p(ticks.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                    ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"megamoe_probe_mfma_rate failed: {rc}")
+        launch(1000)
+        torch.cuda.synchronize()
+        iters = max(1000, int(ms_target * 1e-3 * 2.5e15 / ops_per_iter))
+        tops, mhz = [], []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch(iters)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tops.append(ops_per_iter * iters / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+            t = ticks.view(-1, 2).double().cpu().numpy()
+            mhz.append(float(np.median(t[:, 0] / t[:, 1] * 100.0)))
+        out[kind] = {"TOPS": round(float(np.median(tops)), 1),
+                     "shader_MHz": round(float(np.median(mhz)), 0)}
+    out["what"] = ("back-to-back int8 16x16x64 MFMAs from registers, 16 waves per CU, "
+                   "4x4 accumulator tiles per wave, no memory traffic")
+    return out
+
+
 def _cpu_model() -> str:
+    """Model name, family / model / stepping numbers and logical CPU counts
+    from /proc/cpuinfo (the model name alone can be as short as "AMD EPYC")."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                    info[k] = v
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    return (f"{name} (family {info.get('cpu family', '?')}, model {info.get('model', '?')}, "
+            f"stepping {info.get('stepping', '?')}); {os.cpu_count()} logical CPUs on the "
+            f"host, {len(os.sched_getaffinity(0))} usable by this process")
 
 
 # ---------------------------------------------------------------------------
@@ -349,9 +430,18 @@ def main():
         MM.megamoe_forward(d, dev["x"], dev["expert_idx"], dev["probs"], w1p, dev["scale1"], w2p,
                            dev["scale2"], out, fws)
 
-    # headline: K forward calls, back to back.  The clocks of an idle GPU take
-    # a while to settle under load, so about 0.2 s of untimed forward calls
-    # precede the W counted warm-up steps.
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def flush():
+        flush_buf.fill_(1)  # 512 MiB device write: evicts L2 and the memory-side cache
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # headline: K forward calls, each after a cache flush, each bracketed by
+    # events on the launch stream.  The clocks of an idle GPU take a while to
+    # settle under load, so about 0.2 s of untimed forward calls precede the
+    # W warm-up steps.
     t_pre = time.perf_counter()
     while True:
         for _ in range(4):
@@ -360,29 +450,47 @@ def main():
         if time.perf_counter() - t_pre > 0.2:
             break
     for _ in range(a.warmup):
+        flush()
         fwd()
+    fev = [(ev(), ev()) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        flush()
+        fev[i][0].record(stream)
+        fwd()
+        fev[i][1].record(stream)
+    torch.cuda.synchronize()
+    flushed_wall_s = time.perf_counter() - t0
+    fwd_each = [e0.elapsed_time(e1) for e0, e1 in fev]
+    fwd_ms = float(np.mean(fwd_each))
+
+    # the same forwards back to back, no flush
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(a.steps):
         fwd()
     torch.cuda.synchronize()
-    fwd_ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    b2b_ms = (time.perf_counter() - t0) * 1e3 / a.steps
 
     # per-stage durations: the stages through their own entry points, with
-    # events on the launch stream between them
+    # events on the launch stream between them, each step after a flush
     for _ in range(a.warmup):
+        flush()
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    events = [[ev() for _ in range(6)] for _ in range(a.steps)]
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     for i in range(a.steps):
+        flush()
         step(events[i])
     torch.cuda.synchronize()
-    staged_ms = (time.perf_counter() - t1) * 1e3 / a.steps
     stage_ms = {s: float(np.mean([events[i][j].elapsed_time(events[i][j + 1])
                                   for i in range(a.steps)])) for j, s in enumerate(STAGES)}
     stage_min = {s: float(np.min([events[i][j].elapsed_time(events[i][j + 1])
                                   for i in range(a.steps)])) for j, s in enumerate(STAGES)}
+    staged_ms = float(np.mean([events[i][0].elapsed_time(events[i][5])
+                               for i in range(a.steps)]))
+    del flush_buf
 
     # the forward captured into a HIP graph and replayed
     side = torch.cuda.Stream()
@@ -459,14 +567,23 @@ def main():
         "roofline": roof,
         "gmm_int8_tops": round(gmm_tops, 1),
         "gmm_mfma_frac": round(gmm_tops / PEAK_INT8_TOPS, 4),
-        "step": "one megamoe_forward call (all stages, one stream)",
+        "step": "one megamoe_forward call (all stages, one stream), after a 512 MiB cache flush",
+        "ms_per_step_median": round(float(np.median(fwd_each)), 4),
+        "ms_per_step_min": round(float(np.min(fwd_each)), 4),
+        "timed_wall_s": round(flushed_wall_s, 4),
+        "back_to_back_ms_per_step": round(b2b_ms, 4),
+        "back_to_back_tokens_per_s": round(w.M / (b2b_ms * 1e-3), 1),
         "staged_ms_per_step": round(staged_ms, 4),
         "graph_replay_ms_per_step": round(graph_ms, 4),
         "prepack_ms": round(prepack_ms, 2),
         "stages": stages,
     }
+    if not a.no_mfma_probe:
+        pr = mfma_rate_probe(torch)
+        pr["gmm1_frac_of_random_rate"] = round(stages["gmm1"]["TOPS"] / pr["random"]["TOPS"], 4)
+        res["mfma_rate_probe"] = pr
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(w, inp, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -182,22 +182,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One 16-byte chunk per lane, global -> LDS; lane i writes LDS bytes
 // [lds_base + 16 i, lds_base + 16 i + 16).  lds_base is wave-uniform (M0).
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_base) {
+// The source is a wave-uniform base (a scalar register pair) plus a 32-bit
+// per-lane byte offset, so each copy stream holds one vector register.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds_base) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, off"
+        "global_load_lds_dwordx4 %1, %2"
         :
-        : "s"(lds_base), "v"(gptr)
+        : "s"(lds_base), "v"(voff), "s"(sbase)
         : "memory", "m0");
 }
 
 // The same copy with the non-temporal hint (streamed data: the weights).
-__device__ __forceinline__ void dma16_nt(const void *gptr, uint32_t lds_base) {
+__device__ __forceinline__ void dma16_nt(const void *sbase, uint32_t voff, uint32_t lds_base) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, off nt"
+        "global_load_lds_dwordx4 %1, %2 nt"
         :
-        : "s"(lds_base), "v"(gptr)
+        : "s"(lds_base), "v"(voff), "s"(sbase)
         : "memory", "m0");
 }
 
@@ -326,15 +328,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     const int nst = Kred / kBK64;                    // stages (K slices)
     const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(&smem[0]));
 
-    // LDS byte offsets of this lane's fragment rows inside a stage
-    int fa_off[TM], fb_off[TN];
+    // LDS byte offsets of this lane's fragment rows inside a stage: fragment
+    // i of A starts 16 i rows after fa0 and fragment j of the weights 16 j
+    // rows after fb0 (a row's swizzle depends only on its bits 1-2, which
+    // steps of 16 rows keep), so the other fragments' offsets are constants
+    int fa0, fb0;
     {
-        const int chunk = lane >> 4;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa_off[i] = lds_off64s(wm0 + 16 * i + (lane & 15), chunk);
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            fb_off[j] = BM * kBK64 + lds_off64s(wn0 + 16 * j + (lane & 15), chunk);
+        const int chunk = lane >> 4, r = lane & 15;
+        fa0 = lds_off64s(wm0 + r, chunk);
+        fb0 = BM * kBK64 + lds_off64s(wn0 + r, chunk);
     }
 
     // Round k of workgroup w takes tile k G + w.  When tiles differ in cost
@@ -382,11 +384,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             dma4(p.scale + (size_t)e * N + min(n0 + c * kWave + lane, N - 1),
                  __builtin_amdgcn_readfirstlane(lds_addr(&s_scale[parity][c * kWave])));
 
-        // DMA sources: 1 KB block b = wave + j NW of a stage holds 16 rows;
-        // lane l fills LDS chunk l of the block (row 16 b + (l >> 2), slot
-        // l & 3), taking the chunk that the swizzle puts there.  A rows past
-        // the group's end repeat its last row (their results are not stored).
-        const int8_t *src[LPW];
+        // DMA sources: 1 KB block b = wave + j NW of a stage; lane l fills
+        // 16-byte LDS chunk 64 b + l, taking the chunk that the swizzle puts
+        // there.  A rows past the group's end repeat its last row (their
+        // results are not stored).
+        // per-lane 32-bit source offsets: from p.A for the A rows, from the
+        // tile's first weight block for the weights
+        uint32_t voff[LPW];
         // packed weights are K-slice-major: the block of (expert e, n-block
         // nblk) for K slice ks sits at ((ks * E + e) * NB + nblk) blocks
         const int8_t *btile = p.B + ((size_t)e * NB + nblk) * kPackBlock;
@@ -398,24 +402,26 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
                 const int arow = row0 + min(r, rows - 1);
                 const int srow = p.a_route ? p.a_route[arow] / p.a_div : arow;
-                src[j] = p.A + (size_t)srow * Kred + kc * 16;
+                voff[j] = (uint32_t)srow * (uint32_t)Kred + kc * 16;
             } else {
                 const int q = pch - BM * 4;
                 const int r = q >> 2, kc = (q & 3) ^ swz64(q >> 2);
-                src[j] = btile + r * kBK64 + kc * 16;
+                voff[j] = (uint32_t)(r * kBK64 + kc * 16);
             }
         }
         auto issue = [&](int stage) {
             if (stage >= nst) return;
             const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
+            const int8_t *abase = p.A + (size_t)stage * kBK64;
+            const int8_t *bbase = btile + (size_t)stage * bstep;
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
-                const size_t step = j < kAJ ? (size_t)kBK64 : bstep;
                 const uint32_t dst =
                     __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024));
                 // weights that are read by one tile only (NTB) carry the non-temporal hint
-                if (NTB && j >= kAJ) dma16_nt(src[j] + (size_t)stage * step, dst);
-                else dma16(src[j] + (size_t)stage * step, dst);
+                if (j < kAJ) dma16(abase, voff[j], dst);
+                else if (NTB) dma16_nt(bbase, voff[j], dst);
+                else dma16(bbase, voff[j], dst);
             }
         };
 
@@ -434,11 +440,26 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                     const int8_t *base = smem + (stage % NS) * kStage;
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
-                        xa[i] = *reinterpret_cast<const v4i *>(base + fa_off[i]);
+                        xa[i] = *reinterpret_cast<const v4i *>(base + fa0 + 16 * i * kBK64);
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        xb[j] = *reinterpret_cast<const v4i *>(base + fb_off[j]);
+                        xb[j] = *reinterpret_cast<const v4i *>(base + fb0 + 16 * j * kBK64);
                 }
+            };
+            auto mfmas = [&](const v4i *xa, const v4i *xb) {
+                if constexpr (LIVE) {
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_t(xb[j], xa[i], acc[i][j]);
+                }
+            };
+            // stage kt+1 must have landed; stages up to kt+NS-1 were issued,
+            // the NS-2 after kt+1 may be in flight
+            auto await_next = [&](int kt) {
+                if (kt + NS - 1 < nst) wait_vmcnt<(NS - 2) * LPW>();
+                else wait_vmcnt<0>();
+                __syncthreads();
             };
 #pragma unroll
             for (int st = 0; st < NS; ++st) issue(st);
@@ -460,20 +481,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                             else __builtin_amdgcn_s_setprio(0);
                         }
                     }
-                    // stage kt+1 must have landed; stages up to kt+NS-1 were
-                    // issued, the NS-2 after kt+1 may be in flight
-                    if (kt + NS - 1 < nst) wait_vmcnt<(NS - 2) * LPW>();
-                    else wait_vmcnt<0>();
-                    __syncthreads();
+                    await_next(kt);
                     issue(kt + NS);
                     frag(kt + 1, fa[nxt], fb[nxt]);
-                    if constexpr (LIVE) {
-#pragma unroll
-                        for (int i = 0; i < TM; ++i)
-#pragma unroll
-                            for (int j = 0; j < TN; ++j)
-                                acc[i][j] = mfma_t(fb[cur][j], fa[cur][i], acc[i][j]);
-                    }
+                    mfmas(fa[cur], fb[cur]);
                 });
             }
         };

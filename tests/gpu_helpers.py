@@ -100,3 +100,55 @@ def assert_out_close(gpu_out_f32: np.ndarray, ref_f32: np.ndarray, what: str = "
     err = float(np.abs(gpu_out_f32 - ref_f32).max(initial=0.0))
     assert err <= 2e-2 * scale + 1e-30, f"{what}: max err {err} vs 2e-2*{scale}"
     return err / max(scale, 1e-30)
+
+
+def run_stages_on_oracle_inputs(w, o_ref: dict, dev: dict, w1p, w2p) -> dict:
+    """Each GPU stage fed with the oracle's own inputs to that stage (its gmA,
+    gmC and pts1, q2, gmm2_out and pts2, expanded_row_idx, expert_cumsum), so a
+    difference upstream cannot hide or excuse one downstream: GMM2 is checked
+    on every row even where the GPU's own q2 differs from the oracle's by an
+    LSB.  Returns the GPU results (device tensors)."""
+    d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
+    R = w.R
+    cu = dict(device="cuda")
+
+    def up(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(dtype) if dtype is not None else t).to("cuda")
+
+    cum = up(o_ref["expert_cumsum"])
+    o = dict(
+        acc1=torch.zeros((R, w.N1), dtype=torch.int32, **cu),
+        gmC=torch.zeros((R, w.N1), dtype=torch.float16, **cu),
+        q2=torch.zeros((R, w.I), dtype=torch.int8, **cu),
+        pts2=torch.zeros(R, dtype=torch.float32, **cu),
+        acc2=torch.zeros((R, w.K), dtype=torch.int32, **cu),
+        gmm2_out=torch.zeros((R, w.K), dtype=torch.float16, **cu),
+        out=torch.empty((w.M, w.K), dtype=torch.bfloat16, **cu),
+    )
+    MM.megamoe_gmm1(d, up(o_ref["gmA"]), cum, w1p, dev["scale1"], o["gmC"], o["acc1"])
+    MM.megamoe_swiglu_quant(d, up(o_ref["gmC"]), up(o_ref["pts1"]), cum, o["q2"], o["pts2"])
+    MM.megamoe_gmm2(d, up(o_ref["q2"]), cum, w2p, dev["scale2"], o["gmm2_out"], o["acc2"])
+    MM.megamoe_unpermute(d, up(o_ref["gmm2_out"]), up(o_ref["pts2"]),
+                         up(o_ref["expanded_row_idx"]), dev["probs"], o["out"])
+    return o
+
+
+def compare_stages_on_oracle_inputs(w, o_ref: dict, g: dict) -> None:
+    """Gates for run_stages_on_oracle_inputs: the int32 accumulators and the
+    fp16 GEMM outputs bit-exact on every valid row, q2 within 1 LSB on at most
+    0.1% of elements and pts2 within 1e-6 relative, and the combine + unpermute
+    bit-exact (the same slot-order multiply-then-add in fp32 and the same two
+    round-to-nearest-even bf16 casts as the oracle)."""
+    Rv = w.R - o_ref["dropped"]
+    acc1 = g["acc1"].cpu().numpy()[:Rv]
+    assert np.array_equal(acc1, o_ref["acc1"][:Rv]), "acc1 (oracle gmA)"
+    assert np.array_equal(g["gmC"].cpu().numpy()[:Rv].view(np.uint16),
+                          o_ref["gmC"][:Rv].view(np.uint16)), "gmC (oracle gmA)"
+    assert_int8_within_1lsb(g["q2"].cpu().numpy()[:Rv], o_ref["q2"][:Rv], "q2 (oracle gmC)")
+    np.testing.assert_allclose(g["pts2"].cpu().numpy()[:Rv], o_ref["pts2"][:Rv], rtol=1e-6,
+                               atol=0)
+    assert np.array_equal(g["acc2"].cpu().numpy()[:Rv], o_ref["acc2"][:Rv]), "acc2 (oracle q2)"
+    assert np.array_equal(g["gmm2_out"].cpu().numpy()[:Rv].view(np.uint16),
+                          o_ref["gmm2_out"][:Rv].view(np.uint16)), "gmm2_out (oracle q2)"
+    assert np.array_equal(bf16_bits(g["out"]), o_ref["out"]), "out (oracle gmm2_out, pts2)"

@@ -99,6 +99,7 @@ def test_stages_and_forward_small(w):
     g = H.run_stages(w, dev, w1p, w2p)
     torch.cuda.synchronize()
     _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
     # the fused forward equals the staged run bit for bit
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == o_ref["dropped"]
@@ -109,6 +110,13 @@ def test_stages_and_forward_small(w):
     for k in ("gmC", "gmm2_out"):
         assert torch.equal(g_fast[k].view(torch.int16), g[k].view(torch.int16)), k
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+
+
+def _compare_isolated(w, o_ref, dev, w1p, w2p):
+    """Every stage on the oracle's own inputs to it (see gpu_helpers)."""
+    gi = H.run_stages_on_oracle_inputs(w, o_ref, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    H.compare_stages_on_oracle_inputs(w, o_ref, gi)
 
 
 def _compare_gather(w, g, gg):
@@ -138,6 +146,7 @@ def test_hot_expert_and_duplicates():
     g = H.run_stages(w, dev, w1p, w2p)
     torch.cuda.synchronize()
     _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
 
 
 def test_leftover_tiles_split_by_columns():
@@ -165,6 +174,7 @@ def test_leftover_tiles_split_by_columns():
     g = H.run_stages(w, dev, w1p, w2p)
     torch.cuda.synchronize()
     _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == 0
@@ -209,6 +219,7 @@ def test_trimmed_grid(shape):
     g = H.run_stages(w, dev, w1p, w2p)
     torch.cuda.synchronize()
     _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == 0
@@ -284,6 +295,7 @@ def test_dropped_routes_error_word():
     torch.cuda.synchronize()
     assert g["dropped"] == 3
     _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
     # the error word is reset by the next call
     inp2 = W.generate(w, seed=2)
     dev2 = H.to_dev(inp2)
@@ -335,6 +347,7 @@ def test_random_shapes(case):
     g = H.run_stages(w, dev, w1p, w2p)
     torch.cuda.synchronize()
     _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == o_ref["dropped"]
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
@@ -386,6 +399,7 @@ def test_all_routes_dropped():
     torch.cuda.synchronize()
     assert g["dropped"] == w.R
     _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == w.R
     assert not H.bf16_bits(out).any(), "out must be exactly zero"
@@ -406,6 +420,62 @@ def test_repeat_launch_bit_identical():
         outs.append(H.bf16_bits(out))
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+# ----------------------------------------------------------------------------
+# tile edges: experts whose row counts sit exactly at, one below and one above
+# a GEMM m-block boundary, and the mean rows per expert on both sides of the
+# switch between the 64-row and the 256-row tiles
+# ----------------------------------------------------------------------------
+EDGES = {
+    # 64-row tiles (mean rows per expert <= 52): one and two m-blocks
+    "rows_63_64_65_127_128_129": ([63, 64, 65, 127, 128, 129] + [20] * 10, 512, 256),
+    # 256-row tiles, non-temporal weight copies (mean 53..256)
+    "rows_255_256_257_nt": ([255, 256, 257, 63, 64, 65, 100, 120], 512, 128),
+    # 256-row tiles (mean > 256): one and two m-blocks
+    "rows_255_256_257_511_512_513": ([255, 256, 257, 511, 512, 513, 300, 400], 512, 128),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGES))
+def test_mblock_edges(name):
+    counts, K, I = EDGES[name]
+    E, M = len(counts), sum(counts)
+    w = W.custom(M, K, E, 1, I, name=name)
+    print(f"[parity] {w.describe()} counts {counts} mean {(M + E - 1) // E}", flush=True)
+    inp = W.generate(w, seed=21)
+    ids = np.repeat(np.arange(E), counts).astype(np.int32)
+    inp["expert_idx"][:, 0] = np.random.default_rng(22).permutation(ids)
+    o_ref = O.forward(inp)
+    assert np.array_equal(o_ref["tokens_per_expert"], counts)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
+    _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    out, dropped = H.run_forward(w, dev, w1p, w2p)
+    assert dropped == 0
+    assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
+
+
+@pytest.mark.parametrize("M", [416, 417], ids=["mean52_64row_tiles", "mean53_256row_tiles"])
+def test_tile_switch(M):
+    """E = 8, top_k = 1: 416 routes give 52 mean rows per expert (the last mean
+    the 64-row tiles take), 417 give 53 (the 256-row tiles)."""
+    w = W.custom(M, 512, 8, 1, 256, name=f"switch_M{M}")
+    print(f"[parity] {w.describe()}", flush=True)
+    inp = W.generate(w, seed=23)
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    _compare_isolated(w, o_ref, dev, w1p, w2p)
+    out, dropped = H.run_forward(w, dev, w1p, w2p)
+    assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
 
 
 # ----------------------------------------------------------------------------
@@ -462,33 +532,70 @@ def test_full_size_sampled(name):
     H.assert_int8_within_1lsb(gmA[rows.ravel()], np.repeat(q_ref, w.top_k, axis=0), "gmA")
     assert np.array_equal(pts1[rows.ravel()], np.repeat(s_ref, w.top_k)), "pts1"
 
-    # sampled tokens through the oracle's per-token forward
-    acc1 = g["acc1"]
-    acc2 = g["acc2"]
-    q2_bad = 0
-    q2_total = 0
+    # GEMM and SwiGLU rows, each through the oracle's per-row stage function
+    # on that stage's actual input row (so GMM2 is checked bit for bit even on
+    # a row whose q2 is an LSB away from the oracle's): the first and last row
+    # of every expert group (the m-block edges) and 32 random rows
+    sr = srt["sorted_route"]
+    Rv = int(srt["expert_cumsum"][-1])
+    offs = np.concatenate([[0], srt["expert_cumsum"]])
+    picks = set(np.random.default_rng(3).choice(Rv, size=min(32, Rv), replace=False).tolist())
+    for e in range(w.E):
+        if offs[e + 1] > offs[e]:
+            picks.update((int(offs[e]), int(offs[e + 1]) - 1))
+    gmC_h = g["gmC"].cpu().numpy()
+    q2_h = g["q2"].cpu().numpy()
+    pts2_h = g["pts2"].cpu().numpy()
+    acc1_h = g["acc1"]
+    acc2_h = g["acc2"]
+    g2_h = g["gmm2_out"]
+    flat = inp["expert_idx"].ravel()
+    q2_bad = q2_total = 0
+    for dr in sorted(picks):
+        r = int(sr[dr])
+        e, t = int(flat[r]), r // w.top_k
+        a1, c1 = O.gmm_row(q_ref[t], inp["w1"][e], inp["scale1"][e])
+        assert np.array_equal(acc1_h[dr].cpu().numpy(), a1), f"acc1 row {dr}"
+        assert np.array_equal(gmC_h[dr].view(np.uint16), c1.view(np.uint16)), f"gmC row {dr}"
+        q2r, p2r = O.swiglu_quant_row(gmC_h[dr], pts1[dr])
+        diff = np.abs(q2_h[dr].astype(int) - q2r.astype(int))
+        assert diff.max() <= 1, f"q2 row {dr}"
+        q2_bad += int(np.count_nonzero(diff))
+        q2_total += diff.size
+        np.testing.assert_allclose(pts2_h[dr], p2r, rtol=1e-6)
+        a2, c2 = O.gmm_row(q2_h[dr], inp["w2"][e], inp["scale2"][e])
+        assert np.array_equal(acc2_h[dr].cpu().numpy(), a2), f"acc2 row {dr}"
+        assert np.array_equal(g2_h[dr].cpu().numpy().view(np.uint16), c2.view(np.uint16)), \
+            f"gmm2_out row {dr}"
+    assert q2_bad <= 1e-3 * q2_total, f"q2: {q2_bad}/{q2_total} differ"
+    print(f"[parity-full] {len(picks)} rows through the per-row oracle GEMMs", flush=True)
+
+    # SwiGLU + re-quant on every valid row, from the GPU's own gmC and pts1
+    q2_bad = p2_bad = 0
+    for dr in range(Rv):
+        q2r, p2r = O.swiglu_quant_row(gmC_h[dr], pts1[dr])
+        diff = np.abs(q2_h[dr].astype(np.int32) - q2r.astype(np.int32))
+        assert diff.max() <= 1, f"q2 row {dr}"
+        q2_bad += int(np.count_nonzero(diff))
+        p2_bad += int(pts2_h[dr] != p2r)
+        assert abs(float(pts2_h[dr]) - float(p2r)) <= 1e-6 * abs(float(p2r)), f"pts2 row {dr}"
+    assert q2_bad <= 1e-3 * Rv * w.I, f"q2: {q2_bad} of {Rv * w.I} differ"
+    print(f"[parity-full] SwiGLU on all {Rv} rows: {q2_bad} of {Rv * w.I} q2 codes 1 LSB "
+          f"off, {p2_bad} scales not bit-equal", flush=True)
+
+    # sampled tokens through the oracle's whole per-token forward
     out_gpu = H.bf16_f32(g["out"])
-    errs = []
     ref_rows = []
     got_rows = []
     for t in _sample_tokens(w.M, 6, seed=1):
         ot = O.forward_token(inp, t)
         for s in range(w.top_k):
             dr = int(rows[t, s])
-            assert np.array_equal(acc1[dr].cpu().numpy(), ot["acc1"][s]), f"acc1 t={t} s={s}"
-            assert np.array_equal(g["gmC"][dr].cpu().numpy().view(np.uint16),
-                                  ot["gmC"][s].view(np.uint16)), f"gmC t={t} s={s}"
-            q2g = g["q2"][dr].cpu().numpy()
-            diff = np.abs(q2g.astype(int) - ot["q2"][s].astype(int))
+            assert np.array_equal(acc1_h[dr].cpu().numpy(), ot["acc1"][s]), f"acc1 t={t} s={s}"
+            diff = np.abs(q2_h[dr].astype(int) - ot["q2"][s].astype(int))
             assert diff.max() <= 1
-            q2_bad += int(np.count_nonzero(diff))
-            q2_total += diff.size
-            np.testing.assert_allclose(g["pts2"][dr].item(), ot["pts2"][s], rtol=1e-6)
-            if not diff.any():
-                assert np.array_equal(acc2[dr].cpu().numpy(), ot["acc2"][s]), f"acc2 t={t}"
         ref_rows.append(ot["out_f32"])
         got_rows.append(out_gpu[t])
-    assert q2_bad <= 1e-3 * q2_total, f"q2: {q2_bad}/{q2_total} differ"
     H.assert_out_close(np.stack(got_rows), np.stack(ref_rows))
     # properties that hold at any size
     assert np.all(np.isfinite(out_gpu))
