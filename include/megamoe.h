@@ -110,6 +110,23 @@ int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
                     int32_t *tokens_per_expert, int32_t *expert_cumsum, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* megamoe_permute for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same outputs as megamoe_permute, with no
+ * workspace.  The sort's per-block count table lives in a static device array
+ * of 256 KiB that the library holds per GPU until the process ends, so every
+ * shape megamoe_check_dims accepts fits; a larger table would be rejected with
+ * MEGAMOE_EUNSUPPORTED.  The call allocates nothing.
+ *   dropped  int32 [1] (device, 16-byte aligned): the number of routes whose
+ *            expert id lies outside [0, E), written by this call (the value
+ *            megamoe_last_error reports for the workspace variants).
+ * All calls on one GPU share that array: calls that overlap in time on one GPU
+ * (concurrent streams) race and must be serialised by the caller. */
+int megamoe_permute_noalloc(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                            int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
+                            int32_t *sorted_route, int32_t *tokens_per_expert,
+                            int32_t *expert_cumsum, int32_t *dropped, void *stream);
+
 /* Stage 1 as megamoe_forward runs it: the same sort outputs and pts1 as
  * megamoe_permute, but each token's quantised row is written once,
  * token-major, instead of to every route's row:

@@ -45,6 +45,33 @@ int cu_count_current() {
     return n;
 }
 
+// Scratch of megamoe_permute_noalloc: the sort's per-block expert counts.
+// The sort uses at most 256 blocks of routes and at most 256 experts, so
+// 256 x 256 counts cover every shape megamoe_check_dims accepts.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the name `scratch` is only a stand-in for the symbol: its device address
+// comes from hipGetSymbolAddress (scratch_device_ptr below).
+constexpr size_t kNoAllocScratchBytes = 256u * 256u * sizeof(int32_t);
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (concurrent first calls store the same
+// value).  nullptr if the HIP calls fail.
+int32_t *scratch_device_ptr() {
+    static std::atomic<int32_t *> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    int32_t *p = cached[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+            return nullptr;
+        p = static_cast<int32_t *>(addr);
+        cached[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
 struct Layout {
     size_t err, bcnt, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2, g2, total;
 };
@@ -189,6 +216,25 @@ int megamoe_permute(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
                     size_t ws_bytes, void *stream) {
     return permute_entry(d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
                          expert_cumsum, ws, ws_bytes, false, stream);
+}
+
+int megamoe_permute_noalloc(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
+                            int8_t *gmA, float *pts1, int32_t *eri, int32_t *sorted_route,
+                            int32_t *tokens_per_expert, int32_t *expert_cumsum,
+                            int32_t *dropped, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
+                          expert_cumsum, dropped};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (route_sort_workspace_bytes(d->M * d->top_k, d->E) > kNoAllocScratchBytes)
+        return MEGAMOE_EUNSUPPORTED;
+    int32_t *block_counts = scratch_device_ptr();
+    if (block_counts == nullptr) return MEGAMOE_EHIP;
+    // every count the sort reads is written by the same call first, so the
+    // scratch needs no clearing between calls
+    return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
+                       expert_cumsum, dropped, block_counts, false, (hipStream_t)stream);
 }
 
 int megamoe_permute_tokens(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,

@@ -37,6 +37,7 @@ EXPORTED = [
     "megamoe_strerror", "megamoe_check_dims", "megamoe_workspace_bytes",
     "megamoe_permute_workspace_bytes", "megamoe_packed_weight_bytes", "megamoe_prepack_w1",
     "megamoe_prepack_w2", "megamoe_forward", "megamoe_permute", "megamoe_permute_tokens",
+    "megamoe_permute_noalloc",
     "megamoe_gmm1", "megamoe_gmm1_gather", "megamoe_swiglu_quant", "megamoe_gmm2", "megamoe_unpermute", "megamoe_last_error",
 ]
 
@@ -69,6 +70,8 @@ def load() -> ctypes.CDLL:
     L.megamoe_permute.restype = i32
     L.megamoe_permute_tokens.argtypes = [D, P, P, P, P, P, P, P, P, P, sz, P]
     L.megamoe_permute_tokens.restype = i32
+    L.megamoe_permute_noalloc.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    L.megamoe_permute_noalloc.restype = i32
     L.megamoe_gmm1.argtypes, L.megamoe_gmm1.restype = [D, P, P, P, P, P, P, P], i32
     L.megamoe_gmm1_gather.argtypes = [D, P, P, P, P, P, P, P, P]
     L.megamoe_gmm1_gather.restype = i32
@@ -176,6 +179,15 @@ def megamoe_permute_tokens(d, x, expert_idx, qx, pts1, expanded_row_idx, sorted_
         _ptr(sorted_route, torch.int32), _ptr(tokens_per_expert, torch.int32),
         _ptr(expert_cumsum, torch.int32), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def megamoe_permute_noalloc(d, x, expert_idx, gmA, pts1, expanded_row_idx, sorted_route,
+                            tokens_per_expert, expert_cumsum, dropped, stream=None):
+    _check("megamoe_permute_noalloc", load().megamoe_permute_noalloc(
+        ctypes.byref(d), _ptr(x, torch.float16), _ptr(expert_idx, torch.int32),
+        _ptr(gmA, torch.int8), _ptr(pts1, torch.float32), _ptr(expanded_row_idx, torch.int32),
+        _ptr(sorted_route, torch.int32), _ptr(tokens_per_expert, torch.int32),
+        _ptr(expert_cumsum, torch.int32), _ptr(dropped, torch.int32), _stream(stream)))
 
 
 def megamoe_gmm1_gather(d, qx, sorted_route, expert_cumsum, w1p, scale1, gmC, acc_dbg=None,

@@ -96,6 +96,7 @@ _POINTER_ARGS = {
     "megamoe_forward": (9, ()),               # x .. out, workspace, then its size
     "megamoe_permute": (9, ()),
     "megamoe_permute_tokens": (9, ()),
+    "megamoe_permute_noalloc": (9, ()),
     "megamoe_gmm1": (6, (5,)),
     "megamoe_gmm1_gather": (7, (6,)),
     "megamoe_swiglu_quant": (5, ()),
