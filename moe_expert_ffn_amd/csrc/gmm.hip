@@ -18,7 +18,7 @@
 //  * the grid is persistent (CUs x occupancy workgroups) and deals the tiles
 //    in rounds of one tile per workgroup, backward in odd rounds when costs
 //    differ (a snake, close to a longest-first schedule); a sparse last round
-//    is cut into column pieces;
+//    is cut into row pieces;
 //  * the blockIdx -> position map is XCD-aware: the hardware deals
 //    workgroups round-robin over the 8 XCDs, so positions are assigned so that
 //    each XCD works on a contiguous run of tiles and its own L2 sees the
@@ -347,25 +347,30 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     // expert every round, and some XCDs finished 15% after others.
     auto pos = [&](int k, int w) { return k * G + ((!TRIM && (k & 1)) ? G - 1 - w : w); };
 
-    // When the last round is sparse (L <= G / WAVES_N tiles), each of its tiles is
-    // cut into WAVES_N column pieces (one wave column each).  A piece streams
-    // its tile's copies but only the waves of its columns multiply and store,
-    // so a leftover tile no longer keeps one workgroup busy for a whole tile
-    // after the rest are done.  The pieces of leftover tile j go to WAVES_N
-    // workgroups of one XCD (XCD j % 8), which then share the tile's data in
-    // their L2 (pieces of one tile spread over several XCDs each fetched the
-    // tile from HBM and took longer than the whole tile).  The snake order has
-    // already evened out the full rounds.  A fuller last round keeps the plain
-    // order, whose adjacent tiles share L2 data.
+    // When the last round is sparse (L <= G / WAVES_M tiles), each of its tiles
+    // is cut into WAVES_M row pieces, one per wave row block, so a leftover
+    // tile no longer keeps one workgroup busy for a whole tile after the rest
+    // are done.  Only the waves of a piece's row block multiply and store;
+    // the hardware places wave w on SIMD w % 4, so those WAVES_N waves sit on
+    // different SIMDs and the piece has the whole CU's matrix rate (a cut by
+    // wave columns put a piece's live waves on one SIMD).  A piece copies the
+    // tile's weights for its live waves, and its A copies of the other row
+    // blocks all read its own boundary row, one request per copy instead of
+    // sixteen.  A piece whose row block holds no rows of the tile has nothing
+    // to do.  The pieces of leftover tile j go to WAVES_M workgroups of one
+    // XCD (XCD j % 8), which then share the tile's weights in their L2
+    // (pieces spread over several XCDs each fetched the tile from HBM).  The
+    // snake order has already evened out the full rounds.  A fuller last
+    // round keeps the plain order, whose adjacent tiles share L2 data.
     const int F = total / G, L = total - F * G;
-    const int groups = 8 * (act_xcd / WAVES_N);  // whole groups of WAVES_N slots
+    const int groups = 8 * (act_xcd / WAVES_M);  // whole groups of WAVES_M slots
     const bool ranked = !TRIM && L > 0 && L <= groups;
     int extra = pos(F, vid) < total ? pos(F, vid) : -1, piece = 0;
     if (ranked) {
         const int xcd = vid / act_xcd, slot = vid % act_xcd;
-        const int j = (slot / WAVES_N) * 8 + xcd;  // leftover tile of this group
+        const int j = (slot / WAVES_M) * 8 + xcd;  // leftover tile of this group
         extra = j < L ? F * G + j : -1;
-        piece = slot % WAVES_N;
+        piece = slot % WAVES_M;
     }
 
     int parity = 0;
@@ -378,6 +383,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         const int rows = tr.rows;
         const int n0 = tr.nblk * BN;
         const int nblk = tr.nblk;
+        // a row piece of a leftover tile: rows [plo, phi] of the tile
+        const bool piece_tile = ranked && k == F;
+        const int plo = piece * WM, phi = min(plo + WM, rows) - 1;
+        if (piece_tile && plo >= rows) break;
 
         // scales of the tile's columns (clamped: columns past N are never stored)
         for (int c = wave; c < BN / kWave; c += NW)
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             const int pch = (wave + j * NW) * 64 + lane;
             if (j < kAJ) {
                 const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
-                const int arow = row0 + min(r, rows - 1);
+                const int arow = row0 + (piece_tile ? min(max(r, plo), phi) : min(r, rows - 1));
                 const int srow = p.a_route ? p.a_route[arow] / p.a_div : arow;
                 voff[j] = (uint32_t)srow * (uint32_t)Kred + kc * 16;
             } else {
@@ -488,15 +497,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 });
             }
         };
-        // a column piece of a leftover tile: only its wave column multiplies
+        // a row piece of a leftover tile: only its wave row block multiplies
         // and stores (the other pieces of the tile run on other workgroups)
-        const bool col_live = !ranked || k < F || wave % WAVES_N == piece;
-        if ((!SKIP || wm0 < rows) && col_live) kloop(std::true_type{});
+        const bool piece_live = !piece_tile || wave / WAVES_N == piece;
+        if ((!SKIP || wm0 < rows) && piece_live) kloop(std::true_type{});
         else kloop(std::false_type{});
 
         // every copy of the tile has been awaited inside the loop (the scale
         // copy is older than all of them), and the last barrier published them
-        if (col_live)
+        if (piece_live)
             store_tile_lds<TM, TN>(p, acc, s_scale[parity], row0, rows, n0, wm0, wn0, lane);
     }
 }

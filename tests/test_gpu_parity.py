@@ -149,13 +149,14 @@ def test_hot_expert_and_duplicates():
     _compare_isolated(w, o_ref, dev, w1p, w2p)
 
 
-def test_leftover_tiles_split_by_columns():
+def test_leftover_tiles_split_by_rows():
     """The 256-row GEMM configuration with one full round of tiles and a
-    sparse last round: 256 experts, 20 of them with 300 rows (two m-blocks)
-    and 236 with 130 rows, K = 256 and I = 128 (one n-block in both GEMMs),
-    so each GEMM has 276 tiles for 256 workgroups.  The 20 leftover tiles are
-    cut into column pieces run by different workgroups; every output element
-    is compared with the oracle."""
+    sparse last round: 256 experts, 20 of them with 300 rows (two m-blocks,
+    192 + 108 rows) and 236 with 130 rows, K = 256 and I = 128 (one n-block in
+    both GEMMs), so each GEMM has 276 tiles for 256 workgroups.  The 20
+    leftover tiles (the 108-row ones) are cut into row pieces run by different
+    workgroups: one full row block, one partial, two with no rows; every
+    output element is compared with the oracle."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     hot, cold, E = 20, 236, 256
     M = hot * 300 + cold * 130
