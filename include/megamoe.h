@@ -165,8 +165,8 @@ int megamoe_gmm1_gather(const megamoe_dims *d, const int8_t *qx, const int32_t *
  * Valid rows are [0, expert_cumsum[E-1]).  q2 int8 [R, I], pts2 fp32 [R].
  * silu(u) = u / (1 + exp(-u)) is evaluated with the hardware base-2 exponential
  * and reciprocal plus one correction of the quotient, a few ulp from the IEEE
- * expression (on the decode, large and skewed workloads every q2 code and
- * pts2 equals the IEEE result). */
+ * expression; on every row of the decode, mid, large and skewed workloads each
+ * q2 code and pts2 equals the one from IEEE exp and division. */
 int megamoe_swiglu_quant(const megamoe_dims *d, const uint16_t *gmC, const float *pts1,
                          const int32_t *expert_cumsum, int8_t *q2, float *pts2, void *stream);
 

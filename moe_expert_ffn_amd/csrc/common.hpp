@@ -40,10 +40,9 @@ __device__ __forceinline__ float keep_f32(float v) {
 }
 
 // Two fp32 values -> packed bf16 bits (a in the low half), round to nearest
-// even, by the gfx950 conversion instruction v_cvt_pk_bf16_f32.  Over all 2^32
-// fp32 bit patterns it gives the same bits as rounding the pattern in integer
-// arithmetic (add 0x7fff plus the lowest kept bit, truncate; overflow carries
-// into infinity), with every NaN kept a NaN.
+// even, by the gfx950 conversion instruction v_cvt_pk_bf16_f32.  The unpermute's
+// output is compared bit for bit with the oracle's own round-to-nearest-even
+// conversion on every parity shape.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f2bf_pk(float a, float b) {
