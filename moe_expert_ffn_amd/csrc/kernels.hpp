@@ -36,6 +36,15 @@ hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, in
                                 int32_t *sorted_route, int32_t *tokens_per_expert,
                                 int32_t *expert_cumsum, int32_t *err_word, bool token_major,
                                 hipStream_t stream);
+// The forward's permute for route counts beyond the one-launch path: the
+// route counts and the token-major quantisation in one launch (per-token
+// scales to tscale [M]), then the scatter pass, which also writes pts1.
+hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_idx, int M, int K,
+                                       int E, int top_k, int8_t *qx, float *pts1,
+                                       int32_t *expanded_row_idx, int32_t *sorted_route,
+                                       int32_t *tokens_per_expert, int32_t *expert_cumsum,
+                                       int32_t *err_word, int32_t *block_counts, float *tscale,
+                                       hipStream_t stream);
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
                                 int top_k, int8_t *gmA, float *pts1, bool token_major,
                                 hipStream_t stream);

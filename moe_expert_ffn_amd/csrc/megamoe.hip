@@ -73,12 +73,14 @@ int32_t *scratch_device_ptr() {
 }
 
 struct Layout {
-    size_t err, bcnt, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2, g2, total;
+    size_t err, bcnt, tscale, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2, g2, total;
 };
 
-// permute workspace: error word, then the sort's per-block expert counts
+// permute workspace: error word, the sort's per-block expert counts, then the
+// per-token scales of the token-major path
 size_t permute_ws_bytes(const megamoe_dims &d) {
-    return align_up(kErrBytes) + align_up(route_sort_workspace_bytes(d.M * d.top_k, d.E));
+    return align_up(kErrBytes) + align_up(route_sort_workspace_bytes(d.M * d.top_k, d.E)) +
+           align_up((size_t)d.M * 4);
 }
 
 Layout forward_layout(const megamoe_dims &d) {
@@ -87,6 +89,7 @@ Layout forward_layout(const megamoe_dims &d) {
     size_t o = 0;
     L.err = o;    o += align_up(kErrBytes);
     L.bcnt = o;   o += align_up(route_sort_workspace_bytes((int)R, d.E));
+    L.tscale = o; o += align_up((size_t)d.M * 4);
     L.eri = o;    o += align_up(R * 4);
     L.sorted = o; o += align_up(R * 4);
     L.counts = o; o += align_up((size_t)d.E * 4);
@@ -112,13 +115,20 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_EHI
 
 // token_major: gmA is [M, K] (row t = quantised token t) rather than the
 // expert-sorted [R, K]; the fused forward reads it through the route list.
+// tscale [M] (token_major only): scratch for the per-token scales when the
+// quantisation runs beside the sort's first pass.
 int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_idx, int8_t *gmA,
                 float *pts1, int32_t *eri, int32_t *sorted, int32_t *counts, int32_t *cumsum,
-                int32_t *err_word, int32_t *block_counts, bool token_major, hipStream_t s) {
+                int32_t *err_word, int32_t *block_counts, bool token_major, hipStream_t s,
+                float *tscale = nullptr) {
     const int R = d.M * d.top_k;
     if (permute_fused_ok(R, d.top_k))
         return hip_status(launch_permute_fused(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA, pts1, eri,
                                                sorted, counts, cumsum, err_word, token_major, s));
+    if (token_major && tscale)
+        return hip_status(launch_permute_tokens_2pass(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA,
+                                                      pts1, eri, sorted, counts, cumsum, err_word,
+                                                      block_counts, tscale, s));
     MEGAMOE_TRY(hip_status(launch_route_sort(expert_idx, R, d.E, sorted, eri, counts, cumsum,
                                              err_word, block_counts, s)));
     return hip_status(
@@ -144,9 +154,12 @@ int permute_entry(const megamoe_dims *d, const uint16_t *x, const int32_t *exper
     for (const void *p : ptrs)
         if (!aligned16(p)) return MEGAMOE_EINVAL;
     if (ws_bytes < permute_ws_bytes(*d)) return MEGAMOE_EWORKSPACE;
+    char *w = (char *)ws;
+    const size_t bcnt = align_up(kErrBytes);
+    const size_t tsc = bcnt + align_up(route_sort_workspace_bytes(d->M * d->top_k, d->E));
     return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
-                       expert_cumsum, (int32_t *)ws, (int32_t *)((char *)ws + align_up(kErrBytes)),
-                       token_major, (hipStream_t)stream);
+                       expert_cumsum, (int32_t *)w, (int32_t *)(w + bcnt), token_major,
+                       (hipStream_t)stream, (float *)(w + tsc));
 }
 
 }  // namespace
@@ -330,7 +343,7 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     // expert-sorted rows from them through the route list, so the top_k
     // copies of each token are never written to or re-read from HBM
     MEGAMOE_TRY(run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, bcnt,
-                            true, s));
+                            true, s, (float *)(base + L.tscale)));
     MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s, sorted));
     MEGAMOE_TRY(hip_status(
         launch_swiglu_quant(gmC, pts1, cumsum, d->M * d->top_k, d->E, d->I, q2, pts2, s)));
