@@ -448,14 +448,15 @@ def main():
 
     # headline: K forward calls, each after a cache flush, each bracketed by
     # events on the launch stream.  The clocks of an idle GPU take a while to
-    # settle under load, so about 0.2 s of untimed forward calls precede the
-    # W warm-up steps.
+    # settle under load (with 0.2 s the first timed loop still ran about 3%
+    # slower than the same forwards later in the run), so about 1 s of untimed
+    # forward calls precede the W warm-up steps.
     t_pre = time.perf_counter()
     while True:
         for _ in range(4):
             fwd()
         torch.cuda.synchronize()
-        if time.perf_counter() - t_pre > 0.2:
+        if time.perf_counter() - t_pre > 1.0:
             break
     for _ in range(a.warmup):
         flush()
@@ -472,6 +473,28 @@ def main():
     flushed_wall_s = time.perf_counter() - t0
     fwd_each = [e0.elapsed_time(e1) for e0, e1 in fev]
     fwd_ms = float(np.mean(fwd_each))
+
+    # SwiGLU overlapping GMM1's last round (megamoe_set_overlap(1)) against
+    # the library's default (0): K flushed forwards of each, interleaved
+    # (off, on, on, off, ...) so that clock drift falls on both
+    ov = {0: [], 1: []}
+    try:
+        for i in range(a.steps):
+            for m in ((0, 1) if i % 2 == 0 else (1, 0)):
+                MM.megamoe_set_overlap(m)
+                flush()
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+                fwd()
+                e1.record(stream)
+                ov[m].append((e0, e1))
+        torch.cuda.synchronize()
+    finally:
+        MM.megamoe_set_overlap(0)
+    overlap = {"off_ms": round(float(np.mean([x.elapsed_time(y) for x, y in ov[0]])), 4),
+               "on_ms": round(float(np.mean([x.elapsed_time(y) for x, y in ov[1]])), 4),
+               "what": "flushed forwards, interleaved, with SwiGLU after GMM1 (off, the "
+                       "default) and inside GMM1's last round (on)"}
 
     # the same forwards back to back, no flush
     torch.cuda.synchronize()
@@ -583,6 +606,7 @@ def main():
         "back_to_back_ms_per_step": round(b2b_ms, 4),
         "back_to_back_tokens_per_s": round(w.M / (b2b_ms * 1e-3), 1),
         "staged_ms_per_step": round(staged_ms, 4),
+        "swiglu_overlap": overlap,
         "graph_replay_ms_per_step": round(graph_ms, 4),
         "prepack_ms": round(prepack_ms, 2),
         "stages": stages,

@@ -86,9 +86,10 @@ int megamoe_prepack_w2(const megamoe_dims *d, const int8_t *w2, int8_t *w2p, voi
  *   workspace  >= megamoe_workspace_bytes(); the caller may not touch it while
  *              the forward runs.  Intermediates live there.
  * It runs megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
- * megamoe_gmm2 and megamoe_unpermute in order on the workspace; the result
- * equals, bit for bit, that of the page's five stages (megamoe_permute and
- * megamoe_gmm1 in place of the first two). */
+ * megamoe_gmm2 and megamoe_unpermute in order on the workspace (SwiGLU can
+ * start inside GMM1's last round, see megamoe_set_overlap); the result equals, bit
+ * for bit, that of the page's five stages (megamoe_permute and megamoe_gmm1
+ * in place of the first two). */
 int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
                     const float *probs, const int8_t *w1p, const float *scale1,
                     const int8_t *w2p, const float *scale2, uint16_t *out,
@@ -184,6 +185,21 @@ int megamoe_gmm2(const megamoe_dims *d, const int8_t *q2, const int32_t *expert_
 int megamoe_unpermute(const megamoe_dims *d, const uint16_t *gmm2_out, const float *pts2,
                       const int32_t *expanded_row_idx, const float *probs, uint16_t *out,
                       void *stream);
+
+/* How megamoe_forward runs SwiGLU (the page's overlap of the vector stage with
+ * the matrix stages, "PTO-ISA overlap scheme" and section 4's SwiGLU segments).
+ *   0 (default): GMM1, then SwiGLU on every row;
+ *   1: when GMM1 has at least two full rounds of tiles and a sparse last one,
+ *      the workgroups left without a tile in the last round run SwiGLU on the
+ *      rows whose GMM1 output was complete two rounds earlier, until the
+ *      last-round tiles are done; the SwiGLU kernel does the remaining rows;
+ *   2: as 1, but every workgroup that would wait for the other workgroups
+ *      gives up at once, so the SwiGLU kernel does every row (that path).
+ * On MI355X mode 1 is slower than mode 0 at every workload measured, hence
+ * the default.  The result is bit-identical in all three modes.  The setting
+ * is global to the process and read when megamoe_forward enqueues its work.
+ * Returns MEGAMOE_EINVAL for any other mode. */
+int megamoe_set_overlap(int mode);
 
 /* Synchronises `stream` and reads the number of routes dropped by the last
  * megamoe_permute / megamoe_forward that used this workspace. */

@@ -33,6 +33,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "swiglu_row.hpp"
 
 namespace megamoe {
 
@@ -272,6 +273,145 @@ __device__ __forceinline__ void store_tile_lds(const GmmParams &p, const v4i (&a
     }
 }
 
+// ---------------------------------------------------------------------------
+// SwiGLU in GMM1's last round (the page's overlap of the vector stage with the
+// matrix stages: its SwiGLU segments start as soon as their GMM1 rows exist).
+// With F full rounds and a sparse last round F, the workgroups without a tile
+// in round F run SwiGLU, while the others finish the last tiles, on the rows
+// of m-blocks that have no tile in rounds F - 1 and F.
+//  * Producers never wait: each workgroup, once it has stored its tile of
+//    round F - 2, makes its stores visible at device scope (L2 write-back)
+//    and counts itself in sync[0].  A workgroup that is free in round F has
+//    finished round F - 1 itself, so by then every workgroup has normally
+//    counted itself long before and the wait below ends at once.
+//  * The free workgroups wait until all G have counted themselves (bounded:
+//    tail_spin polls; a workgroup that gives up does no SwiGLU work), then
+//    take 64-row chunks of rows from the counter sync[1], and stop taking
+//    them as soon as every workgroup with a last-round tile has finished
+//    (sync[2]), so that this work never makes GMM1 longer.
+//  * Rows done here get tail_done[row] = 1; the SwiGLU kernel that runs after
+//    GMM1 does every other row.
+// The rows' arithmetic is swiglu_row.hpp, the same as the SwiGLU kernel's.
+// ---------------------------------------------------------------------------
+// What the last-round SwiGLU needs from GmmParams, passed by value (taking
+// the kernel parameter's address would move it to memory for the K loop too).
+struct TailArgs {
+    const uint16_t *C;  // GMM1 output [R, 2I]
+    int8_t *q2;
+    float *pts2;
+    const float *pts1;
+    uint32_t *sync;     // [3]: arrivals, row chunks taken, last-round workgroups done
+    uint8_t *done;
+    int I, spin, E;
+};
+
+__device__ __forceinline__ void tail_arrive(uint32_t *sync) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's tile stores are done
+    __syncthreads();
+    // release at device scope (the L2 write-back covers every wave's stores),
+    // then the count; the counters are accessed at system scope, so their
+    // read-modify-writes from all XCDs meet in memory, not in one XCD's L2
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+__device__ __forceinline__ uint32_t tail_load(const uint32_t *c) {
+    return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Waits for all G arrivals (bounded); true if they all came.
+__device__ __forceinline__ bool tail_wait(const TailArgs &p, int G, int *s_go) {
+    if (threadIdx.x == 0) {
+        int go = 0;
+        if (p.spin >= 0) {
+            for (int n = 0;; ++n) {
+                if (tail_load(p.sync) >= (uint32_t)G) {
+                    go = 1;
+                    break;
+                }
+                if (n >= p.spin) break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        // acquire at device scope: stale lines of other XCDs' stores are
+        // dropped from this CU's L1 and this XCD's L2
+        if (go) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_go = go;
+    }
+    __syncthreads();  // orders the other waves' loads after the acquire
+    return *s_go != 0;
+}
+
+// The part of a 256-row GMM1 workgroup after its tiles.  The schedule values
+// it needs are recomputed here and its arguments come from LDS, so that none
+// of them is kept in registers across the kernel's K loop (the 256-row
+// kernel uses every scalar register there).  The round structure repeats the
+// kernel's: persistent grid of G = gridDim.x workgroups on 8 XCDs, row pieces
+// for a last round of at most G / WAVES_M tiles.
+template <int BM, int WAVES_M, int NW>
+__device__ __forceinline__ void gmm_tail(const TailArgs &p, bool has_last_tile,
+                                         const int (*s_pre)[kMaxE + 1], const int *s_row_off,
+                                         const int *s_rows, int8_t *smem, int *s_go) {
+    if (has_last_tile) {  // done with the last round
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(p.sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        return;
+    }
+    constexpr int UNIT = BM / WAVES_M;
+    const int G = gridDim.x, act_xcd = G >> 3;
+    int total = 0;
+    for (int c = 0; c < WAVES_M; ++c) total += s_pre[c][p.E];
+    const int F = total / G, L = total - F * G;
+    // workgroups with a last-round tile: WAVES_M per leftover tile when it is
+    // cut into row pieces, else one
+    const int n_work = L <= 8 * (act_xcd / WAVES_M) ? L * WAVES_M : L;
+    if (!tail_wait(p, G, s_go)) return;
+
+    uint32_t *bm = reinterpret_cast<uint32_t *>(smem);     // one bit per 64-row unit
+    const int Rv = s_row_off[p.E - 1] + s_rows[p.E - 1];  // valid rows
+    const int nwords = (Rv + 2047) >> 11;                   // <= 4096 (R < 2^23)
+    for (int i = threadIdx.x; i < nwords; i += NW * kWave) bm[i] = 0;
+    __syncthreads();
+    // units holding rows of an m-block with a tile in round F - 1 or F
+    for (int t = (F - 1) * G + (int)threadIdx.x; t < total; t += NW * kWave) {
+        const TileRows tr = tile_rows<BM, UNIT>(t, p.E, s_pre, s_row_off, s_rows);
+        if (tr.rows <= 0) continue;
+        for (int u = tr.row0 >> 6; u <= (tr.row0 + tr.rows - 1) >> 6; ++u)
+            atomicOr(&bm[u >> 5], 1u << (u & 31));
+    }
+    int *s_chunk = s_go;  // reused: the wait's flag has been read
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & (kWave - 1);
+    const int I = p.I;
+    constexpr int kRowsPerWave = 64 / NW;
+    for (;;) {
+        __syncthreads();  // bitmap built / every wave has read the last chunk
+        if (threadIdx.x == 0) {
+            int c = -1;
+            if (tail_load(p.sync + 2) < (uint32_t)n_work)
+                c = (int)__hip_atomic_fetch_add(p.sync + 1, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_SYSTEM);
+            *s_chunk = c;
+        }
+        __syncthreads();
+        const int c = *s_chunk;
+        if (c < 0 || c >= (Rv + 63) >> 6) break;
+        for (int i = 0; i < kRowsPerWave; ++i) {  // wave-uniform rows
+            const int r = c * 64 + wave * kRowsPerWave + i;
+            if (r >= Rv) break;
+            const int u = r >> 6;
+            if ((bm[u >> 5] >> (u & 31)) & 1u) continue;
+            uint4 uraw[4], graw[4];  // I <= 2048: at most 4 chunks of 8 columns per lane
+            swiglu_row_load<4>(p.C + (size_t)r * (2 * I), I, lane, uraw, graw);
+            const float p1 = p.pts1[r];
+            swiglu_row_finish<4>(uraw, graw, p1, I, lane, p.q2 + (size_t)r * I, p.pts2 + r);
+            if (lane == 0) p.done[r] = 1;
+        }
+    }
+}
+
 template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true, int PRIO = 0,
           bool NTB = TRIM>
 __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
@@ -300,6 +440,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     __shared__ int s_pre[U][kMaxE + 1];
     __shared__ int s_row_off[kMaxE];
     __shared__ int s_rows[kMaxE];
+    __shared__ int s_go;
+    __shared__ TailArgs s_targs;  // last-round SwiGLU (GMM1 only)
+    __shared__ int s_tail_round;  // the round after which producers count themselves, or -1
 
     // the wave index is uniform: kept in a scalar register, so that no
     // vector register holds threadIdx across the K loop
@@ -371,6 +514,19 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         const int j = (slot / WAVES_M) * 8 + xcd;  // leftover tile of this group
         extra = j < L ? F * G + j : -1;
         piece = slot % WAVES_M;
+    }
+
+    // SwiGLU in the last round (GMM1 of the forward; tiles of unequal cost).
+    // Kept in LDS and read once per tile: the K loop has no scalar register
+    // to spare.  The K loop's barriers order this write before the reads.
+    if constexpr (!TRIM) {
+        if (threadIdx.x == 0) {
+            // the tail keeps a row's chunks in registers up to I = 2048
+            const bool on = p.tail_q2 != nullptr && F >= 2 && L > 0 && p.tail_I <= 2048;
+            s_tail_round = on ? F - 1 : -1;
+            s_targs = TailArgs{p.C, p.tail_q2, p.tail_pts2, p.tail_pts1, p.tail_sync,
+                               p.tail_done, p.tail_I, p.tail_spin, p.E};
+        }
     }
 
     int parity = 0;
@@ -507,6 +663,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         // copy is older than all of them), and the last barrier published them
         if (piece_live)
             store_tile_lds<TM, TN>(p, acc, s_scale[parity], row0, rows, n0, wm0, wn0, lane);
+        if constexpr (!TRIM) {
+            // done with round F - 2: count this workgroup for the last-round SwiGLU
+            if (k + 1 == __builtin_amdgcn_readfirstlane(s_tail_round)) tail_arrive(s_targs.sync);
+        }
+    }
+
+    if constexpr (!TRIM) {
+        if (__builtin_amdgcn_readfirstlane(s_tail_round) >= 0)
+            gmm_tail<BM, WAVES_M, NW>(s_targs, extra >= 0, s_pre, s_row_off, s_rows, smem, &s_go);
     }
 }
 
@@ -594,6 +759,12 @@ int gmm_pick_variant(int R, int E) {
     // so their copies carry the non-temporal hint; above that, the m-blocks
     // of an expert share each weight block through L2
     return mean <= 256 ? 2 : 1;
+}
+
+bool gmm_tail_ok(int R, int E, int I) {
+    // the 256-row configurations deal tiles of unequal cost (no trimmed
+    // grid), and the tail keeps a row's chunks in registers up to I = 2048
+    return gmm_pick_variant(R, E) != 0 && I <= 2048;
 }
 
 hipError_t launch_gmm(int variant, const GmmParams &prm, int R, int cu_count,

@@ -18,6 +18,16 @@ struct GmmParams {
     // A gathered through the sorted route list)
     const int32_t *a_route = nullptr;
     int a_div = 1;
+    // GMM1 only, nullable tail_q2 = off: workgroups left without a tile in a
+    // sparse last round run SwiGLU on the rows that are already complete
+    // (see gmm.hip).  tail_sync and tail_done must be zero at launch.
+    int8_t *tail_q2 = nullptr;        // [R, tail_I] int8
+    float *tail_pts2 = nullptr;       // [R]
+    const float *tail_pts1 = nullptr; // [R]
+    uint32_t *tail_sync = nullptr;    // [3] counters of the last-round SwiGLU
+    uint8_t *tail_done = nullptr;     // [R] set for each row the last round did
+    int tail_I = 0;
+    int tail_spin = 0;                // poll limit of the wait; < 0: give up at once
 };
 
 // block_counts: device scratch of route_sort_workspace_bytes(R, E) bytes
@@ -35,7 +45,8 @@ hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, in
                                 int top_k, int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
                                 int32_t *sorted_route, int32_t *tokens_per_expert,
                                 int32_t *expert_cumsum, int32_t *err_word, bool token_major,
-                                hipStream_t stream);
+                                hipStream_t stream, uint8_t *tail_done = nullptr,
+                                uint32_t *tail_sync = nullptr);
 // The forward's permute for route counts beyond the one-launch path: the
 // route counts and the token-major quantisation in one launch (per-token
 // scales to tscale [M]), then the scatter pass, which also writes pts1.
@@ -44,13 +55,14 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
                                        int32_t *expanded_row_idx, int32_t *sorted_route,
                                        int32_t *tokens_per_expert, int32_t *expert_cumsum,
                                        int32_t *err_word, int32_t *block_counts, float *tscale,
-                                       hipStream_t stream);
+                                       hipStream_t stream, uint8_t *tail_done = nullptr,
+                                       uint32_t *tail_sync = nullptr);
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
                                 int top_k, int8_t *gmA, float *pts1, bool token_major,
                                 hipStream_t stream);
 hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,
                                const int32_t *expert_cumsum, int R, int E, int I, int8_t *q2,
-                               float *pts2, hipStream_t stream);
+                               float *pts2, hipStream_t stream, const uint8_t *skip = nullptr);
 hipError_t launch_unpermute(const uint16_t *gmm2_out, const float *pts2,
                             const int32_t *expanded_row_idx, const float *probs, int M, int K,
                             int top_k, uint16_t *out, hipStream_t stream);
@@ -59,6 +71,8 @@ hipError_t launch_unpermute(const uint16_t *gmm2_out, const float *pts2,
 size_t packed_weight_bytes(int E, int Kred, int N);
 hipError_t launch_pack(const int8_t *w, int8_t *wp, int E, int Kred, int N, hipStream_t stream);
 int gmm_pick_variant(int R, int E);
+// whether GMM1 at these dims can run SwiGLU in its last round (GmmParams tail_*)
+bool gmm_tail_ok(int R, int E, int I);
 hipError_t launch_gmm(int variant, const GmmParams &prm, int R, int cu_count, hipStream_t stream);
 
 }  // namespace megamoe

@@ -73,7 +73,8 @@ int32_t *scratch_device_ptr() {
 }
 
 struct Layout {
-    size_t err, bcnt, tscale, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2, g2, total;
+    size_t err, bcnt, tscale, tsync, tdone, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2,
+        g2, total;
 };
 
 // permute workspace: error word, the sort's per-block expert counts, then the
@@ -90,6 +91,8 @@ Layout forward_layout(const megamoe_dims &d) {
     L.err = o;    o += align_up(kErrBytes);
     L.bcnt = o;   o += align_up(route_sort_workspace_bytes((int)R, d.E));
     L.tscale = o; o += align_up((size_t)d.M * 4);
+    L.tsync = o;  o += align_up(3 * 4);
+    L.tdone = o;  o += align_up(R);
     L.eri = o;    o += align_up(R * 4);
     L.sorted = o; o += align_up(R * 4);
     L.counts = o; o += align_up((size_t)d.E * 4);
@@ -117,18 +120,23 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MEGAMOE_OK : MEGAMOE_EHI
 // expert-sorted [R, K]; the fused forward reads it through the route list.
 // tscale [M] (token_major only): scratch for the per-token scales when the
 // quantisation runs beside the sort's first pass.
+// tail_done / tail_sync (nullable, forward only): flags of the GMM1 that
+// follows, cleared by the permute's kernels.
 int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_idx, int8_t *gmA,
                 float *pts1, int32_t *eri, int32_t *sorted, int32_t *counts, int32_t *cumsum,
                 int32_t *err_word, int32_t *block_counts, bool token_major, hipStream_t s,
-                float *tscale = nullptr) {
+                float *tscale = nullptr, uint8_t *tail_done = nullptr,
+                uint32_t *tail_sync = nullptr) {
     const int R = d.M * d.top_k;
     if (permute_fused_ok(R, d.top_k))
         return hip_status(launch_permute_fused(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA, pts1, eri,
-                                               sorted, counts, cumsum, err_word, token_major, s));
+                                               sorted, counts, cumsum, err_word, token_major, s,
+                                               tail_done, tail_sync));
     if (token_major && tscale)
         return hip_status(launch_permute_tokens_2pass(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA,
                                                       pts1, eri, sorted, counts, cumsum, err_word,
-                                                      block_counts, tscale, s));
+                                                      block_counts, tscale, s, tail_done,
+                                                      tail_sync));
     MEGAMOE_TRY(hip_status(launch_route_sort(expert_idx, R, d.E, sorted, eri, counts, cumsum,
                                              err_word, block_counts, s)));
     return hip_status(
@@ -136,13 +144,34 @@ int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_
 }
 
 // a_route (nullable): A row d is token a_route[d] / top_k of a token-major A.
+// tail (nullable, GMM1 only): SwiGLU in GMM1's last round, see gmm.hip.
 int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const int8_t *Bp,
             const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s,
-            const int32_t *a_route = nullptr) {
+            const int32_t *a_route = nullptr, const GmmParams *tail = nullptr) {
     const int R = d.M * d.top_k;
     GmmParams prm{A, Bp, scale, cumsum, C, dbg, d.E, N, Kred, a_route, d.top_k};
+    if (tail) {
+        prm.tail_q2 = tail->tail_q2;
+        prm.tail_pts2 = tail->tail_pts2;
+        prm.tail_pts1 = tail->tail_pts1;
+        prm.tail_sync = tail->tail_sync;
+        prm.tail_done = tail->tail_done;
+        prm.tail_I = tail->tail_I;
+        prm.tail_spin = tail->tail_spin;
+    }
     return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
 }
+
+// megamoe_set_overlap: 0 (default) GMM1 then SwiGLU; 1 SwiGLU overlaps
+// GMM1's last round; 2 as 1, with every waiting workgroup giving up at once.
+// Measured on MI355X the overlap is slower (the device-scope L2 write-back it
+// needs, and its HBM traffic beside the last-round tiles, cost more than the
+// SwiGLU time it hides), so it is off unless asked for.
+std::atomic<int> g_overlap{0};
+// poll limit of the wait (each poll is a device-scope load and a short
+// sleep): a workgroup gives up after milliseconds, long after every resident
+// workgroup has arrived (one tile takes at most a few hundred microseconds)
+constexpr int kTailSpin = 8192;
 
 int permute_entry(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
                   int8_t *gmA, float *pts1, int32_t *eri, int32_t *sorted_route,
@@ -339,16 +368,40 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     uint16_t *g2 = (uint16_t *)(base + L.g2);
 
     int32_t *bcnt = (int32_t *)(base + L.bcnt);
+    uint32_t *tsync = (uint32_t *)(base + L.tsync);
+    uint8_t *tdone = (uint8_t *)(base + L.tdone);
+    const int R = d->M * d->top_k;
+    const int overlap = g_overlap.load(std::memory_order_relaxed);
+    const bool tail = overlap != 0 && gmm_tail_ok(R, d->E, d->I);
     // the quantised tokens are written once, token-major; GMM1 gathers its
     // expert-sorted rows from them through the route list, so the top_k
     // copies of each token are never written to or re-read from HBM
     MEGAMOE_TRY(run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, bcnt,
-                            true, s, (float *)(base + L.tscale)));
-    MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s, sorted));
-    MEGAMOE_TRY(hip_status(
-        launch_swiglu_quant(gmC, pts1, cumsum, d->M * d->top_k, d->E, d->I, q2, pts2, s)));
+                            true, s, (float *)(base + L.tscale), tail ? tdone : nullptr,
+                            tail ? tsync : nullptr));
+    // SwiGLU: the rows whose GMM1 output is complete before GMM1's last round
+    // are done by the workgroups left idle in that round; the SwiGLU kernel
+    // does the rest (all rows without the overlap)
+    GmmParams tp{};
+    tp.tail_q2 = q2;
+    tp.tail_pts2 = pts2;
+    tp.tail_pts1 = pts1;
+    tp.tail_sync = tsync;
+    tp.tail_done = tdone;
+    tp.tail_I = d->I;
+    tp.tail_spin = overlap == 2 ? -1 : kTailSpin;
+    MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s, sorted,
+                        tail ? &tp : nullptr));
+    MEGAMOE_TRY(hip_status(launch_swiglu_quant(gmC, pts1, cumsum, R, d->E, d->I, q2, pts2, s,
+                                               tail ? tdone : nullptr)));
     MEGAMOE_TRY(run_gmm(*d, q2, cumsum, w2p, scale2, g2, nullptr, d->K, d->I, s));
     return hip_status(launch_unpermute(g2, pts2, eri, probs, d->M, d->K, d->top_k, out, s));
+}
+
+int megamoe_set_overlap(int mode) {
+    if (mode < 0 || mode > 2) return MEGAMOE_EINVAL;
+    g_overlap.store(mode, std::memory_order_relaxed);
+    return MEGAMOE_OK;
 }
 
 int megamoe_last_error(const void *ws, void *stream, int32_t *bad_route_count) {

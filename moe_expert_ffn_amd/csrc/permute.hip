@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
     const int32_t *__restrict__ block_counts, int32_t *__restrict__ sorted_route,
     int32_t *__restrict__ expanded_row_idx, int32_t *__restrict__ tokens_per_expert,
     int32_t *__restrict__ expert_cumsum, int32_t *__restrict__ err_word,
-    const float *__restrict__ tscale, int top_k, float *__restrict__ pts1) {
+    const float *__restrict__ tscale, int top_k, float *__restrict__ pts1,
+    uint8_t *__restrict__ tail_done, uint32_t *__restrict__ tail_sync) {
     __shared__ int s_base[kMaxExperts];   // next row of each expert for this block
     __shared__ int s_tot[kMaxExperts];
     __shared__ int s_wcnt[kSortWavesB][kMaxExperts];
@@ -161,7 +162,10 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
     __syncthreads();
     const int valid_rows = s_valid;
     if (b == 0) {
-        if (tid == 0) err_word[0] = R - valid_rows;
+        if (tid == 0) {
+            err_word[0] = R - valid_rows;
+            if (tail_sync) tail_sync[0] = tail_sync[1] = tail_sync[2] = 0;
+        }
         for (int d = valid_rows + tid; d < R; d += kSortBlock) sorted_route[d] = -1;
     }
 
@@ -183,6 +187,7 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
             dst = pre + rank;
         }
         if (r < r_end) {
+            if (tail_done) tail_done[r] = 0;  // R flags of the GMM1 that follows
             expanded_row_idx[r] = dst;
             if (dst >= 0) {
                 sorted_route[dst] = r;
@@ -320,7 +325,8 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     int K, int top_k, int8_t *__restrict__ gmA, float *__restrict__ pts1,
     int32_t *__restrict__ expanded_row_idx, int32_t *__restrict__ sorted_route,
     int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_cumsum,
-    int32_t *__restrict__ err_word, bool token_major) {
+    int32_t *__restrict__ err_word, bool token_major, uint8_t *__restrict__ tail_done,
+    uint32_t *__restrict__ tail_sync) {
     __shared__ int h_all[kMaxExperts + 1];
     __shared__ int h_pre[kMaxExperts + 1];
     __shared__ int s_key[kFusedMaxTopK];
@@ -332,6 +338,9 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     const int lane = tid & (kWave - 1);
     const int nchunk = K >> 4;
     const int r_own = t * top_k;
+    // clear the flags of the GMM1 that follows (route r's flag is row r's)
+    if (tail_done && tid < top_k) tail_done[r_own + tid] = 0;
+    if (tail_sync && t == 0 && tid < 3) tail_sync[tid] = 0;
 
     // Every first load is issued up front: the token's row, the first 2048
     // expert ids (all of them up to R = 2048) and the token's own ids.
@@ -484,14 +493,14 @@ hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, in
                                 int top_k, int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
                                 int32_t *sorted_route, int32_t *tokens_per_expert,
                                 int32_t *expert_cumsum, int32_t *err_word, bool token_major,
-                                hipStream_t stream) {
+                                hipStream_t stream, uint8_t *tail_done, uint32_t *tail_sync) {
     const int R = M * top_k;
     const int per_thread = (K / 16 + 255) / 256;
     dim3 grid(M), block(256);
 #define MEGAMOE_PERMUTE_FUSED(C)                                                              \
     hipLaunchKernelGGL(permute_fused_kernel<C>, grid, block, 0, stream, x, expert_idx, R, E, K, \
                        top_k, gmA, pts1, expanded_row_idx, sorted_route, tokens_per_expert,     \
-                       expert_cumsum, err_word, token_major)
+                       expert_cumsum, err_word, token_major, tail_done, tail_sync)
     if (per_thread <= 1) MEGAMOE_PERMUTE_FUSED(1);
     else if (per_thread <= 2) MEGAMOE_PERMUTE_FUSED(2);
     else if (per_thread <= 4) MEGAMOE_PERMUTE_FUSED(4);
@@ -527,7 +536,8 @@ hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *s
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(route_scatter_kernel, dim3(B), dim3(kSortBlock), 0, stream, expert_idx, R,
                        E, C, nbits, B, block_counts, sorted_route, expanded_row_idx,
-                       tokens_per_expert, expert_cumsum, err_word, nullptr, 1, nullptr);
+                       tokens_per_expert, expert_cumsum, err_word, nullptr, 1, nullptr, nullptr,
+                       nullptr);
     return hipGetLastError();
 }
 
@@ -536,7 +546,8 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
                                        int32_t *expanded_row_idx, int32_t *sorted_route,
                                        int32_t *tokens_per_expert, int32_t *expert_cumsum,
                                        int32_t *err_word, int32_t *block_counts, float *tscale,
-                                       hipStream_t stream) {
+                                       hipStream_t stream, uint8_t *tail_done,
+                                       uint32_t *tail_sync) {
     const int R = M * top_k;
     int nbits = 0;
     while ((1 << nbits) <= E) ++nbits;  // keys 0..E (E = dropped)
@@ -556,7 +567,8 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(route_scatter_kernel, dim3(B), dim3(kSortBlock), 0, stream, expert_idx, R,
                        E, C, nbits, B, block_counts, sorted_route, expanded_row_idx,
-                       tokens_per_expert, expert_cumsum, err_word, tscale, top_k, pts1);
+                       tokens_per_expert, expert_cumsum, err_word, tscale, top_k, pts1, tail_done,
+                       tail_sync);
     return hipGetLastError();
 }
 

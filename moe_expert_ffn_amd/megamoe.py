@@ -39,6 +39,7 @@ EXPORTED = [
     "megamoe_prepack_w2", "megamoe_forward", "megamoe_permute", "megamoe_permute_tokens",
     "megamoe_permute_noalloc",
     "megamoe_gmm1", "megamoe_gmm1_gather", "megamoe_swiglu_quant", "megamoe_gmm2", "megamoe_unpermute", "megamoe_last_error",
+    "megamoe_set_overlap",
 ]
 
 _lib = None
@@ -81,6 +82,7 @@ def load() -> ctypes.CDLL:
     L.megamoe_unpermute.argtypes, L.megamoe_unpermute.restype = [D, P, P, P, P, P, P], i32
     L.megamoe_last_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
     L.megamoe_last_error.restype = i32
+    L.megamoe_set_overlap.argtypes, L.megamoe_set_overlap.restype = [i32], i32
     _lib = L
     return L
 
@@ -231,6 +233,12 @@ def megamoe_last_error(workspace, stream=None) -> int:
     _check("megamoe_last_error", load().megamoe_last_error(_ptr(workspace), _stream(stream),
                                                            ctypes.byref(v)))
     return v.value
+
+
+def megamoe_set_overlap(mode: int) -> None:
+    """0: GMM1 then SwiGLU (default); 1: SwiGLU overlaps GMM1's last round;
+    2: as 1, with the overlap's waits giving up at once (its fallback path)."""
+    _check("megamoe_set_overlap", load().megamoe_set_overlap(int(mode)))
 
 
 class MegaMoE:

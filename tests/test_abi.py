@@ -82,6 +82,14 @@ def test_null_and_misaligned_pointers_rejected():
     assert rc == 3
 
 
+def test_set_overlap_modes():
+    lib = MM.load()
+    for bad in (-1, 3, 1 << 20):
+        assert lib.megamoe_set_overlap(bad) == 1
+    for mode in (1, 2, 0):  # ends on the default
+        assert lib.megamoe_set_overlap(mode) == 0
+
+
 def test_strerror():
     assert MM.strerror(0) == "ok"
     assert "workspace" in MM.strerror(3)

@@ -182,6 +182,50 @@ def test_leftover_tiles_split_by_rows():
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
 
 
+@pytest.mark.parametrize("hot,I,branch", [(20, 256, "pieces"), (25, 384, "plain_odd"),
+                                          (50, 256, "plain_even")])
+def test_overlap_modes_bit_identical(hot, I, branch):
+    """SwiGLU inside GMM1's last round (megamoe_set_overlap): the forward is
+    bit-identical with the overlap off (0), on (1) and forced to give up (2),
+    and equal to the staged path, whose every stage matches the oracle.
+    256 experts, `hot` with 300 rows and the rest with 130, top_k = 1, so
+    GMM1 (I / 128 n-blocks) has at least two full rounds and a sparse last
+    round.  The shapes reach the three layouts of that round: row pieces (at
+    most a quarter full), and the plain order after an odd and after an even
+    number of full rounds."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    E = 256
+    cold = E - hot
+    M = hot * 300 + cold * 130
+    w = W.custom(M, 256, E, 1, I, name=f"overlap_{branch}")
+    tiles = (hot * 2 + cold) * (2 * I // 256)
+    G = (min(cus, M // 256 + E) + 7) // 8 * 8
+    F, L = tiles // G, tiles % G
+    assert F >= 2 and L >= 1, f"no sparse last round after two full ones on {cus} CUs"
+    want = {"pieces": 4 * L <= G, "plain_odd": 4 * L > G and F % 2 == 1,
+            "plain_even": 4 * L > G and F % 2 == 0}[branch]
+    assert want, f"shape does not reach the {branch} branch on {cus} CUs (F={F}, L={L})"
+    print(f"[parity] {w.describe()} GMM1 tiles {tiles} on {G} workgroups", flush=True)
+    inp = W.generate(w, seed=6)
+    ids = np.concatenate([np.repeat(np.arange(hot), 300), hot + np.repeat(np.arange(cold), 130)])
+    inp["expert_idx"][:, 0] = np.random.default_rng(7).permutation(ids).astype(np.int32)
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    ref_bits = H.bf16_bits(g["out"])
+    try:
+        for mode in (1, 0, 2, 1):
+            MM.megamoe_set_overlap(mode)
+            out, dropped = H.run_forward(w, dev, w1p, w2p)
+            assert dropped == 0
+            assert np.array_equal(H.bf16_bits(out), ref_bits), f"overlap mode {mode}"
+    finally:
+        MM.megamoe_set_overlap(0)
+
+
 def _stream_tiles(R: int, E: int, N: int, counts: np.ndarray, cus: int):
     """Tile count and launch grid of the 64-row GEMM configuration (two
     workgroups per CU), as the library computes them."""
