@@ -45,7 +45,7 @@ RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
 # (BM, WAVES_M, WAVES_N, NS, TRIM, SKIP, PRIO, NTB): (VGPRs, AGPRs).  The
 # 256-row tiles run 16 waves per CU, so 128 registers per wave is the ceiling.
 GEMM_REGISTERS = {
-    (64, 1, 4, 3, 1, 1, 16, 1): (94, 92),
+    (64, 1, 4, 3, 1, 1, 16, 1): (102, 92),
     (256, 4, 4, 4, 0, 1, 0, 0): (124, 0),
     (256, 4, 4, 4, 0, 1, 0, 1): (124, 0),
 }

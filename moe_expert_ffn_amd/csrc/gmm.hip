@@ -529,25 +529,40 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         }
     }
 
-    int parity = 0;
-    for (int k = 0;; ++k, parity ^= 1) {
-        const int t = k < F ? pos(k, vid) : (k == F ? extra : -1);
-        if (t < 0) break;
+    // A tile's set-up: its rows, the DMA source offsets, and the copy of its
+    // scales into LDS slot par.  The set-up of tile k + 1 runs between tile
+    // k's K loop and its epilogue, so that tile k's output stores and tile
+    // k + 1's first copies are in flight together (vector memory operations
+    // complete in issue order, so a set-up after the stores would wait for
+    // them before its own loads and copies).
+    struct TileSetup {
+        int valid, e, row0, rows, n0;
+        bool piece_tile;
+        const int8_t *btile;
+        uint32_t voff[LPW];
+    };
+    // packed weights are K-slice-major: the block of (expert e, n-block
+    // nblk) for K slice ks sits at ((ks * E + e) * NB + nblk) blocks
+    const size_t bstep = (size_t)p.E * NB * kPackBlock;
+    auto setup = [&](int kk, int par) {
+        TileSetup ts{};
+        const int t = kk < F ? pos(kk, vid) : (kk == F ? extra : -1);
+        if (t < 0) return ts;
         const TileRows tr = tile_rows<BM, BM / WAVES_M>(t, p.E, s_pre, s_row_off, s_rows);
-        const int e = tr.e;
-        const int row0 = tr.row0;
-        const int rows = tr.rows;
-        const int n0 = tr.nblk * BN;
-        const int nblk = tr.nblk;
+        ts.e = tr.e;
+        ts.row0 = tr.row0;
+        ts.rows = tr.rows;
+        ts.n0 = tr.nblk * BN;
         // a row piece of a leftover tile: rows [plo, phi] of the tile
-        const bool piece_tile = ranked && k == F;
-        const int plo = piece * WM, phi = min(plo + WM, rows) - 1;
-        if (piece_tile && plo >= rows) break;
+        ts.piece_tile = ranked && kk == F;
+        const int plo = piece * WM, phi = min(plo + WM, tr.rows) - 1;
+        if (ts.piece_tile && plo >= tr.rows) return ts;
+        ts.valid = 1;
 
         // scales of the tile's columns (clamped: columns past N are never stored)
         for (int c = wave; c < BN / kWave; c += NW)
-            dma4(p.scale + (size_t)e * N + min(n0 + c * kWave + lane, N - 1),
-                 __builtin_amdgcn_readfirstlane(lds_addr(&s_scale[parity][c * kWave])));
+            dma4(p.scale + (size_t)tr.e * N + min(ts.n0 + c * kWave + lane, N - 1),
+                 __builtin_amdgcn_readfirstlane(lds_addr(&s_scale[par][c * kWave])));
 
         // DMA sources: 1 KB block b = wave + j NW of a stage; lane l fills
         // 16-byte LDS chunk 64 b + l, taking the chunk that the swizzle puts
@@ -555,38 +570,43 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         // results are not stored).
         // per-lane 32-bit source offsets: from p.A for the A rows, from the
         // tile's first weight block for the weights
-        uint32_t voff[LPW];
-        // packed weights are K-slice-major: the block of (expert e, n-block
-        // nblk) for K slice ks sits at ((ks * E + e) * NB + nblk) blocks
-        const int8_t *btile = p.B + ((size_t)e * NB + nblk) * kPackBlock;
-        const size_t bstep = (size_t)p.E * NB * kPackBlock;
+        ts.btile = p.B + ((size_t)tr.e * NB + tr.nblk) * kPackBlock;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int pch = (wave + j * NW) * 64 + lane;
             if (j < kAJ) {
                 const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
-                const int arow = row0 + (piece_tile ? min(max(r, plo), phi) : min(r, rows - 1));
+                const int arow =
+                    tr.row0 + (ts.piece_tile ? min(max(r, plo), phi) : min(r, tr.rows - 1));
                 const int srow = p.a_route ? p.a_route[arow] / p.a_div : arow;
-                voff[j] = (uint32_t)srow * (uint32_t)Kred + kc * 16;
+                ts.voff[j] = (uint32_t)srow * (uint32_t)Kred + kc * 16;
             } else {
                 const int q = pch - BM * 4;
                 const int r = q >> 2, kc = (q & 3) ^ swz64(q >> 2);
-                voff[j] = (uint32_t)(r * kBK64 + kc * 16);
+                ts.voff[j] = (uint32_t)(r * kBK64 + kc * 16);
             }
         }
+        return ts;
+    };
+
+    int parity = 0;
+    TileSetup cur = setup(0, 0);
+    for (int k = 0; cur.valid; ++k, parity ^= 1) {
+        const int row0 = cur.row0, rows = cur.rows, n0 = cur.n0;
+        const bool piece_tile = cur.piece_tile;
         auto issue = [&](int stage) {
             if (stage >= nst) return;
             const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
             const int8_t *abase = p.A + (size_t)stage * kBK64;
-            const int8_t *bbase = btile + (size_t)stage * bstep;
+            const int8_t *bbase = cur.btile + (size_t)stage * bstep;
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
                 const uint32_t dst =
                     __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024));
                 // weights that are read by one tile only (NTB) carry the non-temporal hint
-                if (j < kAJ) dma16(abase, voff[j], dst);
-                else if (NTB) dma16_nt(bbase, voff[j], dst);
-                else dma16(bbase, voff[j], dst);
+                if (j < kAJ) dma16(abase, cur.voff[j], dst);
+                else if (NTB) dma16_nt(bbase, cur.voff[j], dst);
+                else dma16(bbase, cur.voff[j], dst);
             }
         };
 
@@ -659,6 +679,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         if ((!SKIP || wm0 < rows) && piece_live) kloop(std::true_type{});
         else kloop(std::false_type{});
 
+        // the next tile's set-up (its scale copy goes to the other LDS slot)
+        const TileSetup nxt = setup(k + 1, parity ^ 1);
         // every copy of the tile has been awaited inside the loop (the scale
         // copy is older than all of them), and the last barrier published them
         if (piece_live)
@@ -667,6 +689,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             // done with round F - 2: count this workgroup for the last-round SwiGLU
             if (k + 1 == __builtin_amdgcn_readfirstlane(s_tail_round)) tail_arrive(s_targs.sync);
         }
+        cur = nxt;
     }
 
     if constexpr (!TRIM) {
