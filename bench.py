@@ -8,7 +8,7 @@ single-GPU forward (M=2048, K=7168, E=32, top-k 8, I=2048), where the grouped
 GEMMs are bound by the int8 matrix cores; --workload picks decode, mid, skewed
 or skewed_empty instead.  Prints ONE JSON line.
 
-Timing.  The headline step is one megamoe_forward call.  About 0.2 s of
+Timing.  The headline step is one megamoe_forward call.  About 1 s of
 untimed calls come first (the clocks of an idle GPU take that long to settle
 under load), then W untimed steps, then K timed steps.  Before every timed
 step a 512 MiB device write flushes the L2 caches and the 256 MB memory-side
@@ -23,7 +23,9 @@ calls the stage entry points megamoe_forward is made of
 (megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
 megamoe_gmm2, megamoe_unpermute) -- the same kernels, in the same order --
 with HIP events recorded on the launch stream between the stages.  The
-forward captured into a HIP graph and replayed is timed as well.
+forward captured into a HIP graph and replayed is timed as well, and so are
+flushed forwards with SwiGLU inside GMM1's last round (megamoe_set_overlap),
+interleaved with the default ones.
 """
 from __future__ import annotations
 
@@ -49,8 +51,10 @@ STAGES = ["permute", "gmm1", "swiglu", "gmm2", "unpermute"]
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 100 flushed steps take about 0.1 s at large: long enough to average over
+    # the clock swings of a few tens of milliseconds seen between 20-step loops
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -58,6 +62,8 @@ def parse():
                     help="CPU time budget of each leg of the oracle baseline")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the matrix-core rate probe reported beside the roofline")
+    ap.add_argument("--no-overlap-ab", action="store_true",
+                    help="skip the interleaved overlap on/off loop (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profile", default=None, metavar="TRACE_DIR",
@@ -90,8 +96,15 @@ def algorithmic(w, counts: np.ndarray) -> dict:
 
 
 def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source and of the headers beside it (every kernel
+    includes some of them), so that a change to either invalidates a
+    profile taken from the older code."""
+    h = hashlib.sha256()
+    d = os.path.dirname(path)
+    for p in [path] + sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hpp")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(kernel_src: str, workload: str, stage: str):
@@ -215,9 +228,13 @@ def _cpu_model() -> str:
 # rocprofv3 summaries (no GPU needed): kernel-trace stats and HBM traffic
 # ---------------------------------------------------------------------------
 STAGE_OF_KERNEL = {"route_count_kernel": "permute", "route_scatter_kernel": "permute",
-                   "quant_scatter_kernel": "permute", "permute_fused_kernel": "permute",
+                   "count_quant_kernel": "permute", "quant_scatter_kernel": "permute",
+                   "permute_fused_kernel": "permute",
                    "swiglu_quant_kernel": "swiglu", "unpermute_kernel": "unpermute"}
-PERMUTE_LAST = ("quant_scatter_kernel", "permute_fused_kernel")
+# the permute's last launch, after which the GEMM is GMM1: the quantiser of the
+# three-launch path, the one-launch path, or the scatter of the forward's
+# two-launch path
+PERMUTE_LAST = ("quant_scatter_kernel", "permute_fused_kernel", "route_scatter_kernel")
 CALIB_BYTES = 1 << 30
 
 
@@ -267,11 +284,22 @@ def summarize_profile(a):
     w = W.WORKLOADS[a.workload]
     trace = _csv_rows(_find(a.summarize_profile, "kernel_trace.csv"))
     stats = _csv_rows(_find(a.summarize_profile, "kernel_stats.csv"))
-    per_stage = {}
+    # every dispatch, and those of steps that follow a cache flush (the
+    # flush ends with a reduction over a 512 MiB buffer)
+    per_stage, flushed = {}, {}
+    after_flush = False
     for r, name, stage in _label_dispatches(trace):
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if name == "reduce_kernel":
+            after_flush = True
+            continue
         per_stage.setdefault(stage, []).append(dur)
+        if after_flush and stage in STAGES:
+            flushed.setdefault(stage, []).append(dur)
+        if stage == "unpermute":
+            after_flush = False
     steps = max(1, len(per_stage.get("gmm1", [])))
+    fsteps = max(1, len(flushed.get("gmm1", [])))
     lines = [f"# rocprofv3 kernel trace: {w.describe()}", "",
              "Command (from the repository root):", "", "```", a.command or "(not recorded)", "```",
              "", "## rocprofv3 --stats (kernel_stats.csv)", "",
@@ -281,11 +309,17 @@ def summarize_profile(a):
                      f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
                      f"{float(r['Percentage']):.1f} |")
     lines += ["", "## per pipeline stage and step (from the dispatch trace)", "",
-              "| stage | kernel launches per step | us per step |", "|---|---|---|"]
+              f"All {steps} steps of the run (most of them the untimed back-to-back forwards "
+              f"that let the clocks settle), and the {fsteps} steps that follow a cache "
+              "flush (the timed and warm-up steps of the flushed loops).", "",
+              "| stage | kernel launches per step | us per step, all steps | "
+              "us per step, flushed steps |", "|---|---|---|---|"]
     for st in STAGES:
         v = per_stage.get(st, [])
+        fv = flushed.get(st, [])
         if v:
-            lines.append(f"| {st} | {len(v) / steps:g} | {np.sum(v) / steps:.1f} |")
+            fl = f"{np.sum(fv) / fsteps:.1f}" if fv else "-"
+            lines.append(f"| {st} | {len(v) / steps:g} | {np.sum(v) / steps:.1f} | {fl} |")
     traffic = {}
     if a.pmc_fetch and a.pmc_write:
         def counter_avg(d, cname):
@@ -479,7 +513,7 @@ def main():
     # (off, on, on, off, ...) so that clock drift falls on both
     ov = {0: [], 1: []}
     try:
-        for i in range(a.steps):
+        for i in range(0 if a.no_overlap_ab else a.steps):
             for m in ((0, 1) if i % 2 == 0 else (1, 0)):
                 MM.megamoe_set_overlap(m)
                 flush()
@@ -491,10 +525,11 @@ def main():
         torch.cuda.synchronize()
     finally:
         MM.megamoe_set_overlap(0)
-    overlap = {"off_ms": round(float(np.mean([x.elapsed_time(y) for x, y in ov[0]])), 4),
-               "on_ms": round(float(np.mean([x.elapsed_time(y) for x, y in ov[1]])), 4),
-               "what": "flushed forwards, interleaved, with SwiGLU after GMM1 (off, the "
-                       "default) and inside GMM1's last round (on)"}
+    overlap = None if a.no_overlap_ab else {
+        "off_ms": round(float(np.mean([x.elapsed_time(y) for x, y in ov[0]])), 4),
+        "on_ms": round(float(np.mean([x.elapsed_time(y) for x, y in ov[1]])), 4),
+        "what": "flushed forwards, interleaved, with SwiGLU after GMM1 (off, the default) "
+                "and inside GMM1's last round (on)"}
 
     # the same forwards back to back, no flush
     torch.cuda.synchronize()
