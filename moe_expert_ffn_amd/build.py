@@ -8,9 +8,10 @@ The build also guards the grouped GEMM's register budget.  Its K loop issues
 the global -> LDS copies from inline assembly, which the compiler's wait-count
 pass does not see; any compiler-visible vector load that lands in the loop (a
 spill reload, for instance) gets a wait that in hardware also waits for every
-copy in flight and drains the copy ring.  Every instantiation of the GEMM
-kernel must therefore compile with no spills and with no more registers than
-recorded in GEMM_REGISTERS below; the build fails otherwise.
+copy in flight and drains the copy ring.  The build therefore compiles the
+GEMM to assembly as well and fails if any scratch (spill) access lies inside
+a loop that issues those copies, or if an instantiation uses more registers
+or spills more values than recorded in GEMM_RESOURCES below.
 """
 from __future__ import annotations
 
@@ -42,13 +43,16 @@ HIPFLAGS = [
 RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
 
 # Registers of each GEMM tile configuration, keyed by its template arguments
-# (BM, WAVES_M, WAVES_N, NS, TRIM, SKIP, PRIO, NTB): (VGPRs, AGPRs).  The
-# 256-row tiles run 16 waves per CU, so 128 registers per wave is the ceiling.
-GEMM_REGISTERS = {
-    (64, 1, 4, 3, 1, 1, 16, 1): (102, 92),
-    (256, 4, 4, 4, 0, 1, 0, 0): (124, 0),
-    (256, 4, 4, 4, 0, 1, 0, 1): (124, 0),
+# (BM, WAVES_M, WAVES_N, NS, TRIM, SKIP, PRIO, NTB): (VGPRs, AGPRs, spilled
+# values).  The 256-row tiles run 16 waves per CU, so 128 registers per wave
+# is the ceiling; their few spilled values are tile set-up values stored
+# before a tile's copies and reloaded after its K loop (checked below).
+GEMM_RESOURCES = {
+    (64, 1, 4, 3, 1, 1, 16, 1): (110, 92, 0),
+    (256, 4, 4, 4, 0, 1, 0, 0): (128, 0, 6),
+    (256, 4, 4, 4, 0, 1, 0, 1): (128, 0, 6),
 }
+GEMM_SRC = os.path.join(CSRC, "gmm.hip")
 
 
 def _compile(src: str) -> tuple[str, str]:
@@ -85,7 +89,7 @@ def gemm_template_args(name: str):
 
 
 def check_gemm_resources(remarks: str) -> list[str]:
-    """Every GEMM instantiation: no spills, registers within the record."""
+    """Every GEMM instantiation: registers and spills within the record."""
     problems = []
     found = 0
     for name, r in kernel_resources(remarks).items():
@@ -93,31 +97,82 @@ def check_gemm_resources(remarks: str) -> list[str]:
         if key is None:
             continue
         found += 1
-        spills = r.get("VGPRs Spill", 0) + r.get("SGPRs Spill", 0)
-        if spills:
-            problems.append(f"GEMM {key}: {spills} spilled registers")
-        rec = GEMM_REGISTERS.get(key)
-        got = (r.get("VGPRs", 0), r.get("AGPRs", 0))
+        got = (r.get("VGPRs", 0), r.get("AGPRs", 0),
+               r.get("VGPRs Spill", 0) + r.get("SGPRs Spill", 0))
+        rec = GEMM_RESOURCES.get(key)
         if rec is None:
-            problems.append(f"GEMM {key}: no register record (VGPRs {got[0]}, AGPRs {got[1]})")
-        elif got[0] > rec[0] or got[1] > rec[1]:
-            problems.append(f"GEMM {key}: VGPRs {got[0]}, AGPRs {got[1]} above the record "
-                            f"{rec[0]}, {rec[1]}")
+            problems.append(f"GEMM {key}: no record (VGPRs {got[0]}, AGPRs {got[1]}, "
+                            f"spills {got[2]})")
+        elif any(g > r_ for g, r_ in zip(got, rec)):
+            problems.append(f"GEMM {key}: VGPRs {got[0]}, AGPRs {got[1]}, spills {got[2]} "
+                            f"above the record {rec[0]}, {rec[1]}, {rec[2]}")
     if not found:
         problems.append("no GEMM kernel found in the resource report")
     return problems
 
 
+def check_gemm_loops(asm: str) -> list[str]:
+    """No scratch access inside a loop that issues global -> LDS copies.
+
+    The device assembly marks each basic block with its loop depth.  The
+    GEMM's tile loop is depth 1 and its K loops, nested in it, are depth 2 or
+    more; every run of nested blocks that contains a copy
+    (global_load_lds_dwordx4) must contain no scratch_ instruction."""
+    problems = []
+    found = 0
+    for func in asm.split("; -- Begin function ")[1:]:
+        name = func.split("\n", 1)[0].strip()
+        if "gmm_i8_ring_kernel" not in name:
+            continue
+        found += 1
+        depth, region = 0, []
+
+        def close():
+            if (any("global_load_lds_dwordx4" in x for x in region)
+                    and any("scratch_" in x for x in region)):
+                problems.append(f"GEMM {gemm_template_args(name)}: a spill access inside a "
+                                "loop that issues the ring copies")
+
+        for line in func.split(".Lfunc_end", 1)[0].splitlines():
+            d = None
+            m = re.search(r"Depth=(\d+)", line)
+            if line.startswith(".LBB") or (m and "Loop Header" in line):
+                d = int(m.group(1)) if m else 0
+            if d is not None:
+                if d < 2 and depth >= 2:
+                    close()
+                    region = []
+                depth = d
+            if depth >= 2:
+                region.append(line)
+        close()
+    if not found:
+        problems.append("no GEMM kernel found in the assembly")
+    return problems
+
+
+def _gemm_asm() -> str:
+    out = os.path.join(BUILD, "gmm.s")
+    cmd = [HIPCC, *HIPFLAGS, "-S", "--cuda-device-only", GEMM_SRC, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {GEMM_SRC}:\n{r.stderr}")
+    with open(out) as f:
+        return f.read()
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        asm = ex.submit(_gemm_asm)
         done = list(ex.map(_compile, srcs))
+        gemm_asm = asm.result()
     objs = [o for o, _ in done]
     remarks = "\n".join(r for _, r in done)
     with open(os.path.join(BUILD, "resource_usage.txt"), "w") as f:
         f.write(remarks)
-    problems = check_gemm_resources(remarks)
+    problems = check_gemm_resources(remarks) + check_gemm_loops(gemm_asm)
     if problems:
         raise RuntimeError("GEMM register guard failed:\n  " + "\n  ".join(problems))
     tmp = LIB + f".tmp{os.getpid()}"

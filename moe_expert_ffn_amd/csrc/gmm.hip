@@ -247,28 +247,18 @@ __device__ __forceinline__ void dma4(const void *gptr, uint32_t lds_base) {
 // live row blocks costs about r / WAVES_M of a full one in MFMA time.
 // ---------------------------------------------------------------------------
 template <int TM, int TN>
-__device__ __forceinline__ void store_tile_lds(const GmmParams &p, const v4i (&acc)[TM][TN],
-                                               const float *s_sc, int row0, int rows, int n0,
-                                               int wm0, int wn0, int lane) {
+__device__ __forceinline__ void store_acc_dbg(const GmmParams &p, const v4i (&acc)[TM][TN], int row0,
+                                              int rows, int n0, int wm0, int wn0, int lane) {
     const int N = p.N;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int cl = wn0 + 16 * j + 4 * (lane >> 4);
-        const int col = n0 + cl;
+        const int col = n0 + wn0 + 16 * j + 4 * (lane >> 4);
         if (col >= N) continue;  // N is a multiple of 16, so col + 3 < N here
-        const float4 s4 = *reinterpret_cast<const float4 *>(s_sc + cl);
-        const float s[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int rl = wm0 + 16 * i + (lane & 15);
             if (rl >= rows) continue;
-            const size_t idx = (size_t)(row0 + rl) * N + col;
-            uint32_t h[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) h[v] = f2h(keep_f32((float)acc[i][j][v] * s[v]));
-            *reinterpret_cast<uint2 *>(p.C + idx) =
-                make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-            if (p.acc_dbg) *reinterpret_cast<v4i *>(p.acc_dbg + idx) = acc[i][j];
+            *reinterpret_cast<v4i *>(p.acc_dbg + (size_t)(row0 + rl) * N + col) = acc[i][j];
         }
     }
 }
@@ -412,6 +402,53 @@ __device__ __forceinline__ void gmm_tail(const TailArgs &p, bool has_last_tile,
     }
 }
 
+// The epilogue through LDS.  Written straight from the MFMA layout, each
+// store instruction covers 32 bytes of 16 rows, so every 128-byte line of
+// the output took four partial writes.  Vector memory operations complete in
+// issue order, so the next tile's first copies waited for all of them (a
+// timing-only build without the stores ran GMM2 at large 27% faster).  Here
+// the waves first write the dequantised fp16 tile into the ring (free after
+// the K loop), rows of BN fp16 with 16-byte chunk c of row r at chunk
+// c ^ (r & 31), which keeps both the 8-byte writes of 16 rows and the
+// 16-byte reads along a row free of bank conflicts; then every wave stores
+// two whole rows per instruction (1 KB, full lines).  Rows [r_lo, r_hi) of
+// the tile are stored; live: this wave's accumulators hold tile rows.
+template <int TM, int TN, int NW>
+__device__ __forceinline__ void store_tile_coalesced(const GmmParams &p, const v4i (&acc)[TM][TN],
+                                                     const float *s_sc, int row0, int n0,
+                                                     int wm0, int wn0, int lane, int wave,
+                                                     int8_t *buf, int r_lo, int r_hi, bool live) {
+    constexpr int RB = kPackRows * 2;  // bytes of one tile row
+    __syncthreads();                   // every wave is done with the ring
+    if (live) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int cl = wn0 + 16 * j + 4 * (lane >> 4);
+            const float4 s4 = *reinterpret_cast<const float4 *>(s_sc + cl);
+            const float s[4] = {s4.x, s4.y, s4.z, s4.w};
+            const int chunk = cl >> 3, half = (cl >> 2) & 1;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int rl = wm0 + 16 * i + (lane & 15);
+                uint32_t h[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) h[v] = f2h(keep_f32((float)acc[i][j][v] * s[v]));
+                *reinterpret_cast<uint2 *>(buf + rl * RB + ((chunk ^ (rl & 31)) << 4) +
+                                           (half << 3)) =
+                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+        }
+    }
+    __syncthreads();
+    const int c = lane & 31;  // 16-byte chunk of a row: columns 8 c .. 8 c + 7
+    const bool col_ok = n0 + 8 * c < p.N;  // N is a multiple of 128
+    for (int r = r_lo + 2 * wave + (lane >> 5); r < r_hi; r += 2 * NW) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(buf + r * RB + ((c ^ (r & 31)) << 4));
+        if (col_ok) store_nt16(p.C + (size_t)(row0 + r) * p.N + n0 + 8 * c, v);
+    }
+    __syncthreads();  // the ring is free again for the next tile's copies
+}
+
 template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true, int PRIO = 0,
           bool NTB = TRIM>
 __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(GmmParams p) {
@@ -443,6 +480,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     __shared__ int s_go;
     __shared__ TailArgs s_targs;  // last-round SwiGLU (GMM1 only)
     __shared__ int s_tail_round;  // the round after which producers count themselves, or -1
+    // what the epilogue needs of each tile (row0, rows, n0, first and end row
+    // stored, row piece): kept in LDS by tile parity, not in registers
+    // across the K loop, which uses every scalar register
+    __shared__ int s_tile[2][6];
 
     // the wave index is uniform: kept in a scalar register, so that no
     // vector register holds threadIdx across the K loop
@@ -558,6 +599,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         const int plo = piece * WM, phi = min(plo + WM, tr.rows) - 1;
         if (ts.piece_tile && plo >= tr.rows) return ts;
         ts.valid = 1;
+        if (threadIdx.x == 0) {
+            s_tile[par][0] = tr.row0;
+            s_tile[par][1] = tr.rows;
+            s_tile[par][2] = ts.n0;
+            s_tile[par][3] = ts.piece_tile ? plo : 0;
+            s_tile[par][4] = ts.piece_tile ? phi + 1 : min(tr.rows, BM);
+            s_tile[par][5] = ts.piece_tile;
+        }
 
         // scales of the tile's columns (clamped: columns past N are never stored)
         for (int c = wave; c < BN / kWave; c += NW)
@@ -592,7 +641,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     int parity = 0;
     TileSetup cur = setup(0, 0);
     for (int k = 0; cur.valid; ++k, parity ^= 1) {
-        const int row0 = cur.row0, rows = cur.rows, n0 = cur.n0;
+        const int rows = cur.rows;
         const bool piece_tile = cur.piece_tile;
         auto issue = [&](int stage) {
             if (stage >= nst) return;
@@ -682,9 +731,23 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         // the next tile's set-up (its scale copy goes to the other LDS slot)
         const TileSetup nxt = setup(k + 1, parity ^ 1);
         // every copy of the tile has been awaited inside the loop (the scale
-        // copy is older than all of them), and the last barrier published them
-        if (piece_live)
-            store_tile_lds<TM, TN>(p, acc, s_scale[parity], row0, rows, n0, wm0, wn0, lane);
+        // copy is older than all of them), and the last barrier published them.
+        // The int32 accumulators of the debug output go straight from the
+        // registers, and the fp16 tile with them.
+        static_assert(BM * kPackRows * 2 <= NS * kStage, "the fp16 tile fits in the ring");
+        {
+            const int t_row0 = __builtin_amdgcn_readfirstlane(s_tile[parity][0]);
+            const int t_rows = __builtin_amdgcn_readfirstlane(s_tile[parity][1]);
+            const int t_n0 = __builtin_amdgcn_readfirstlane(s_tile[parity][2]);
+            const int r_lo = __builtin_amdgcn_readfirstlane(s_tile[parity][3]);
+            const int r_hi = __builtin_amdgcn_readfirstlane(s_tile[parity][4]);
+            const bool t_piece = __builtin_amdgcn_readfirstlane(s_tile[parity][5]) != 0;
+            const bool live = (!t_piece || wave / WAVES_N == piece) && wm0 < t_rows;
+            if (p.acc_dbg && live)
+                store_acc_dbg<TM, TN>(p, acc, t_row0, t_rows, t_n0, wm0, wn0, lane);
+            store_tile_coalesced<TM, TN, NW>(p, acc, s_scale[parity], t_row0, t_n0, wm0, wn0, lane,
+                                             wave, smem, r_lo, r_hi, live);
+        }
         if constexpr (!TRIM) {
             // done with round F - 2: count this workgroup for the last-round SwiGLU
             if (k + 1 == __builtin_amdgcn_readfirstlane(s_tail_round)) tail_arrive(s_targs.sync);
