@@ -42,18 +42,85 @@ __device__ __forceinline__ int route_key(const int32_t *__restrict__ expert_idx,
     return (e >= 0 && e < E) ? e : E;  // E marks a dropped route
 }
 
-// CAST_ROUND(x / scale), clamped to [-127, 127], for x an fp16 value of a row
-// whose largest |x| is amax (also fp16), scale = amax / 127 and inv = 1 / scale
-// (both IEEE).  The quotient is x * inv corrected once by its FMA residual,
-// q + inv * (x - q * scale) (Markstein's method), three instructions instead
-// of the ten of an IEEE division.  For every finite fp16 amax > 0 and every
-// fp16 x with |x| <= amax it yields the same integer as roundf of the IEEE
-// quotient: all 2^31 such pairs were checked on the GPU.
+// CAST_ROUND(x / scale) for x an fp16 value of a row whose largest |x| is amax
+// (also fp16), scale = amax / 127 and inv = 1 / scale (both IEEE; inv = 0 for
+// an all-zero row, which gives 0 everywhere).
+//  * The quotient is x * inv corrected once by its FMA residual,
+//    q + inv * (x - q * scale) (Markstein's method): three instructions instead
+//    of the ten of an IEEE division.  The first product is an FMA with a +0
+//    addend so that the hardware reads x as fp16 in the same instruction.
+//  * Half away from zero is the truncation of q + copysign(0.49999997, q), the
+//    largest float below one half (adding exactly one half would take
+//    0.49999997 itself to 1), and the truncation is the float -> int
+//    conversion: two instructions and the conversion instead of the six of
+//    roundf.  |x| <= amax keeps the sum within (-127.5, 127.5), so no clamp
+//    is needed.
+// For every finite fp16 amax > 0 and every fp16 x with |x| <= amax this gives
+// the same integer as roundf of the IEEE quotient, clamped to [-127, 127];
+// tests/csrc/quant_exhaustive.c checks all 1,007,681,535 such pairs.
 __device__ __forceinline__ int quant_round(float x, float scale, float inv) {
-    const float q0 = x * inv;
+    const float q0 = __builtin_fmaf(x, inv, 0.0f);
     const float q = __builtin_fmaf(__builtin_fmaf(-q0, scale, x), inv, q0);
-    const float r = roundf(q);  // half away from zero
-    return (int)fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)(q + __builtin_copysignf(0x1.fffffep-2f, q));
+}
+
+// 8 fp16 values (one 16-byte word) -> 8 int8 codes.  The low bytes of four
+// codes are gathered into a word by three byte permutes.
+__device__ __forceinline__ uint2 quant_chunk8(const uint4 &raw, float scale, float inv) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw);
+    uint32_t packed[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        int q[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int idx = j * 4 + h;  // element within the 8-element chunk
+            const uint16_t bits = (uint16_t)((w[idx >> 1] >> ((idx & 1) * 16)) & 0xffffu);
+            q[h] = quant_round(h2f(bits), scale, inv);
+        }
+        // bytes [q0, q1, 0, 0] and [q2, q3, 0, 0], then [q0, q1, q2, q3]
+        const uint32_t lo = __builtin_amdgcn_perm((uint32_t)q[1], (uint32_t)q[0], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm((uint32_t)q[3], (uint32_t)q[2], 0x0c0c0400u);
+        packed[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+// 16 fp16 values (two 16-byte words) -> 16 int8 codes.
+__device__ __forceinline__ uint4 quant_chunk16(const uint4 (&raw)[2], float scale, float inv) {
+    const uint2 a = quant_chunk8(raw[0], scale, inv), b = quant_chunk8(raw[1], scale, inv);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// The largest |x| over 16-byte words of fp16 values, as fp16 bits.  With the
+// sign bits cleared, finite fp16 values order like their bit patterns, so the
+// maximum takes one packed 16-bit integer max per two values.  (The
+// quantiser's inputs are finite; a NaN would be taken as the maximum.)
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2_t absmax_step(u16x2_t m, const uint4 &raw) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[j] & 0x7fff7fffu));
+    return m;
+}
+// ... over a thread's 16-element chunks c = tid + 256 i < nchunk
+template <int MAXC>
+__device__ __forceinline__ uint32_t chunks_absmax_bits(const uint4 (&raw)[MAXC][2], int tid,
+                                                       int nchunk) {
+    u16x2_t m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+        if (tid + i * 256 < nchunk) m = absmax_step(absmax_step(m, raw[i][0]), raw[i][1]);
+    return m[0] > m[1] ? m[0] : m[1];
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
 }
 
 // Pass 1: histogram of the expert ids of routes [b*C, (b+1)*C) of block b.
@@ -109,6 +176,18 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
     const int b = blockIdx.x;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 
+    // this thread's first route key and its token's scale are requested
+    // before the table is read, so the two round trips overlap
+    const int r_end = min(R, (b + 1) * C);
+    int key_next = E;
+    float ts_next = 0.0f;
+    {
+        const int r = b * C + tid;
+        if (r < r_end) {
+            key_next = route_key(expert_idx, r, R, E);
+            if (tscale) ts_next = tscale[r / top_k];
+        }
+    }
     for (int e = tid; e < E; e += kSortBlock) {
         s_tot[e] = 0;
         s_base[e] = 0;
@@ -169,12 +248,17 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
         for (int d = valid_rows + tid; d < R; d += kSortBlock) sorted_route[d] = -1;
     }
 
-    const int r_end = min(R, (b + 1) * C);
     for (int r0 = b * C; r0 < r_end; r0 += kSortBlock) {
         for (int i = tid; i < kSortWavesB * kMaxExperts; i += kSortBlock) (&s_wcnt[0][0])[i] = 0;
         __syncthreads();
-        const int r = r0 + wave * kWave + lane;
-        const int key = (r < r_end) ? route_key(expert_idx, r, R, E) : E;
+        const int r = r0 + tid;  // tid = wave * kWave + lane
+        const int key = key_next;
+        const float ts = ts_next;
+        key_next = E;  // the next round's key and scale
+        if (r + kSortBlock < r_end) {
+            key_next = route_key(expert_idx, r + kSortBlock, R, E);
+            if (tscale) ts_next = tscale[(r + kSortBlock) / top_k];
+        }
         const bool ok = key < E;
         const uint64_t m = match_key(key, __ballot(ok), nbits);
         const int rank = __popcll(m & below);
@@ -191,7 +275,7 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
             expanded_row_idx[r] = dst;
             if (dst >= 0) {
                 sorted_route[dst] = r;
-                if (tscale) pts1[dst] = tscale[r / top_k];
+                if (tscale) pts1[dst] = ts;
             }
         }
         __syncthreads();
@@ -207,62 +291,51 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
 
 // One workgroup per token.  Each thread owns 16-element chunks of the row
 // (two 16-byte loads of fp16, one 16-byte int8 store per destination row).
-// tscale (nullable, token-major only): the token's scale goes to tscale[t]
-// instead of to its routes' rows (the sort has not run yet).
-template <int MAXC>
-__device__ __forceinline__ void quant_token(const uint16_t *__restrict__ x,
-                                            const int32_t *__restrict__ expanded_row_idx, int K,
-                                            int top_k, int8_t *__restrict__ gmA,
-                                            float *__restrict__ pts1, bool token_major, int t,
-                                            float *__restrict__ tscale) {
-    __shared__ float s_red[4];
-    const int tid = threadIdx.x;
-    const int nchunk = K >> 4;
-    const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)t * K);
+// When the chunks do not fill every thread the same number of times, the
+// lighter wave moves with the token (slot), so no SIMD always gets it.
+__device__ __forceinline__ int quant_slot(int t) { return ((int)threadIdx.x + ((t & 3) << 6)) & 255; }
 
-    uint4 raw[MAXC][2];
-    float amax = 0.0f;
+template <int MAXC>
+__device__ __forceinline__ void quant_token_load(const uint16_t *__restrict__ x, int K, int t,
+                                                 uint4 (&raw)[MAXC][2]) {
+    const int slot = quant_slot(t), nchunk = K >> 4;
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)t * K);
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
+        const int c = slot + i * 256;
         if (c < nchunk) {
             raw[i][0] = load_nt16(xr + 2 * c);  // x is read once
             raw[i][1] = load_nt16(xr + 2 * c + 1);
-            const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] & 0xffffu))));
-                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] >> 16))));
-            }
         }
     }
-    amax = wave_max(amax);
-    if ((tid & 63) == 0) s_red[tid >> 6] = amax;
+}
+
+// tscale (nullable, token-major only): the token's scale goes to tscale[t]
+// instead of to its routes' rows (the sort has not run yet).
+template <int MAXC>
+__device__ __forceinline__ void quant_token_finish(const uint4 (&raw)[MAXC][2],
+                                                   const int32_t *__restrict__ expanded_row_idx,
+                                                   int K, int top_k, int8_t *__restrict__ gmA,
+                                                   float *__restrict__ pts1, bool token_major,
+                                                   int t, float *__restrict__ tscale) {
+    __shared__ uint32_t s_red[4];
+    const int tid = threadIdx.x;
+    const int slot = quant_slot(t), nchunk = K >> 4;
+    const uint32_t mbits = wave_max_u32(chunks_absmax_bits<MAXC>(raw, slot, nchunk));
+    if ((tid & 63) == 0) s_red[tid >> 6] = mbits;
     __syncthreads();
-    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const uint32_t m01 = s_red[0] > s_red[1] ? s_red[0] : s_red[1];
+    const uint32_t m23 = s_red[2] > s_red[3] ? s_red[2] : s_red[3];
+    const float amax = h2f((uint16_t)(m01 > m23 ? m01 : m23));
     const float scale = amax / 127.0f;  // per-token dynamic scale
-    const float inv = 1.0f / scale;
+    const float inv = amax != 0.0f ? 1.0f / scale : 0.0f;
 
     const int32_t *rows = token_major ? nullptr : expanded_row_idx + (size_t)t * top_k;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
+        const int c = slot + i * 256;
         if (c >= nchunk) continue;
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
-        uint32_t packed[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int idx = j * 4 + h;  // element within the 16-element chunk
-                const uint16_t bits = (uint16_t)((w[idx >> 1] >> ((idx & 1) * 16)) & 0xffffu);
-                const int q = amax != 0.0f ? quant_round(h2f(bits), scale, inv) : 0;
-                word |= ((uint32_t)q & 0xffu) << (8 * h);
-            }
-            packed[j] = word;
-        }
-        const uint4 out = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        const uint4 out = quant_chunk16(raw[i], scale, inv);
         if (token_major) {
             *reinterpret_cast<uint4 *>(gmA + (size_t)t * K + (size_t)c * 16) = out;
         } else {
@@ -288,22 +361,32 @@ template <int MAXC>
 __global__ __launch_bounds__(256) void quant_scatter_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ expanded_row_idx, int K,
     int top_k, int8_t *__restrict__ gmA, float *__restrict__ pts1, bool token_major) {
-    quant_token<MAXC>(x, expanded_row_idx, K, top_k, gmA, pts1, token_major, blockIdx.x, nullptr);
+    uint4 raw[MAXC][2];
+    quant_token_load<MAXC>(x, K, blockIdx.x, raw);
+    quant_token_finish<MAXC>(raw, expanded_row_idx, K, top_k, gmA, pts1, token_major, blockIdx.x,
+                             nullptr);
 }
 
-// The forward's first launch for large route counts: workgroups [0, B) count
-// the expert ids of their route block (sort pass 1), workgroups B.. each
-// quantise one token to its token-major row and its scale to tscale.  The two
-// are independent, so one launch runs both; the scatter pass then writes each
-// route row's pts1 from tscale.  (One wave per token, four tokens per
-// workgroup, measured slower: 17.1 against 14.1 us at M = 2048, K = 7168.)
+// The forward's first launch for large route counts: workgroup b quantises
+// token b (if b < M) to its token-major row and its scale to tscale, and
+// counts the expert ids of route block b (if b < B; sort pass 1).  The two are
+// independent, so one launch runs both; the scatter pass then writes each
+// route row's pts1 from tscale.  A workgroup requests its x row before it
+// counts, so the two latencies overlap.  Giving the count its own workgroups
+// put M + B workgroups in the launch: at M = 2048 the last 64 no longer fit
+// the GPU at once (8 per CU) and started only as others ended.  (One wave per
+// token, four tokens per workgroup, was slower too: 17.1 against 14.1 us at
+// M = 2048, K = 7168.)
 template <int MAXC>
 __global__ __launch_bounds__(256) void count_quant_kernel(
     const int32_t *__restrict__ expert_idx, int R, int E, int C, int B,
-    int32_t *__restrict__ block_counts, const uint16_t *__restrict__ x, int K,
+    int32_t *__restrict__ block_counts, const uint16_t *__restrict__ x, int M, int K,
     int8_t *__restrict__ qx, float *__restrict__ tscale) {
-    if ((int)blockIdx.x < B) route_count_block(expert_idx, R, E, C, blockIdx.x, block_counts);
-    else quant_token<MAXC>(x, nullptr, K, 1, qx, nullptr, true, blockIdx.x - B, tscale);
+    const int b = blockIdx.x;
+    uint4 raw[MAXC][2];
+    if (b < M) quant_token_load<MAXC>(x, K, b, raw);
+    if (b < B) route_count_block(expert_idx, R, E, C, b, block_counts);
+    if (b < M) quant_token_finish<MAXC>(raw, nullptr, K, 1, qx, nullptr, true, b, tscale);
 }
 
 // Small route counts: the whole of FrontReorder in one launch, one workgroup
@@ -331,7 +414,7 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     __shared__ int h_pre[kMaxExperts + 1];
     __shared__ int s_key[kFusedMaxTopK];
     __shared__ int s_dst[kFusedMaxTopK];
-    __shared__ float s_red[4];
+    __shared__ uint32_t s_red[4];
     __shared__ int s_valid;
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -364,25 +447,14 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     }
 
     // the row's absolute maximum
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-        const int c = tid + i * 256;
-        if (c < nchunk) {
-            const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] & 0xffffu))));
-                amax = fmaxf(amax, fabsf(h2f((uint16_t)(w[j] >> 16))));
-            }
-        }
-    }
-    amax = wave_max(amax);
-    if (lane == 0) s_red[tid >> 6] = amax;
+    const uint32_t mbits = wave_max_u32(chunks_absmax_bits<MAXC>(raw, tid, nchunk));
+    if (lane == 0) s_red[tid >> 6] = mbits;
     __syncthreads();  // counters zeroed; s_key and s_red written
-    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const uint32_t m01 = s_red[0] > s_red[1] ? s_red[0] : s_red[1];
+    const uint32_t m23 = s_red[2] > s_red[3] ? s_red[2] : s_red[3];
+    const float amax = h2f((uint16_t)(m01 > m23 ? m01 : m23));
     const float scale = amax / 127.0f;
-    const float inv = 1.0f / scale;
+    const float inv = amax != 0.0f ? 1.0f / scale : 0.0f;
 
     // histograms: every route's expert, and the routes before this token's
     // (key E, a dropped route, is counted too, in slot E)
@@ -408,21 +480,7 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     for (int i = 0; i < MAXC; ++i) {
         const int c = tid + i * 256;
         if (c >= nchunk) continue;
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[i][0]);
-        uint32_t packed[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int idx = j * 4 + h;
-                const uint16_t bits = (uint16_t)((w[idx >> 1] >> ((idx & 1) * 16)) & 0xffffu);
-                const int qv = amax != 0.0f ? quant_round(h2f(bits), scale, inv) : 0;
-                word |= ((uint32_t)qv & 0xffu) << (8 * h);
-            }
-            packed[j] = word;
-        }
-        q[i] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        q[i] = quant_chunk16(raw[i], scale, inv);
         if (token_major) *reinterpret_cast<uint4 *>(gmA + (size_t)t * K + (size_t)c * 16) = q[i];
     }
     __syncthreads();  // histograms complete
@@ -554,10 +612,10 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
     const int C = route_sort_chunk(R);
     const int B = (R + C - 1) / C;
     const int per_thread = (K / 16 + 255) / 256;  // K <= 32768: at most 8
-    dim3 grid(B + M), block(256);
+    dim3 grid(max(B, M)), block(256);
 #define MEGAMOE_COUNT_QUANT(MC)                                                                \
     hipLaunchKernelGGL(count_quant_kernel<MC>, grid, block, 0, stream, expert_idx, R, E, C, B, \
-                       block_counts, x, K, qx, tscale)
+                       block_counts, x, M, K, qx, tscale)
     if (per_thread <= 1) MEGAMOE_COUNT_QUANT(1);
     else if (per_thread <= 2) MEGAMOE_COUNT_QUANT(2);
     else if (per_thread <= 4) MEGAMOE_COUNT_QUANT(4);
@@ -575,7 +633,7 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
                                 int top_k, int8_t *gmA, float *pts1, bool token_major,
                                 hipStream_t stream) {
-    const int per_thread = (K / 16 + 255) / 256;
+    const int per_thread = (K / 16 + 255) / 256;  // K <= 32768: at most 8
     dim3 grid(M), block(256);
     if (per_thread <= 1)
         hipLaunchKernelGGL(quant_scatter_kernel<1>, grid, block, 0, stream, x, expanded_row_idx, K,
