@@ -72,8 +72,14 @@ __device__ __forceinline__ void swiglu_row_finish(const uint4 (&uraw)[MAXC],
             const uint32_t *gw = reinterpret_cast<const uint32_t *>(&graw[i]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float u = h2f((uint16_t)((uw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;
-                const float g = h2f((uint16_t)((gw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)) * p1;
+                // u = fp32(u16) * p1 as an FMA with a +0 addend, so that the
+                // hardware reads the fp16 value in the same instruction (the
+                // product and its rounding are the same; only a -0 becomes +0,
+                // which gives a zero y either way)
+                const float u = __builtin_fmaf(
+                    h2f((uint16_t)((uw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)), p1, 0.0f);
+                const float g = __builtin_fmaf(
+                    h2f((uint16_t)((gw[j >> 1] >> ((j & 1) * 16)) & 0xffffu)), p1, 0.0f);
                 const float v = silu_times(u, g);
                 y[i][j] = v;
                 amax = fmaxf(amax, fabsf(v));
@@ -82,24 +88,27 @@ __device__ __forceinline__ void swiglu_row_finish(const uint4 (&uraw)[MAXC],
     }
     amax = wave_max(amax);
     const float scale2 = amax / 127.0f;
-    const float mul = 127.0f / amax;
+    const float mul = amax != 0.0f ? 127.0f / amax : 0.0f;  // an all-zero row gives 0
 
+    // CAST_RINT(y * mul): the product is rounded to fp32 first, then adding
+    // 1.5 * 2^23 rounds it to an integer, to nearest even, in the low bits of
+    // the sum (|y * mul| <= 127 * (1 + 2^-23) < 2^22, so the sum has unit
+    // spacing); the low byte of those bits is the int8 code.  |y| <= max|y|
+    // keeps the code within [-127, 127], so no clamp is needed.
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
         const int c = lane + i * kWave;
         if (c >= nchunk) continue;
-        uint32_t lo = 0, hi = 0;
+        uint32_t b[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            int q = 0;
-            if (amax != 0.0f) {
-                float r = rintf(y[i][j] * mul);  // CAST_RINT: ties to even
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                q = (int)r;
-            }
-            if (j < 4) lo |= ((uint32_t)q & 0xffu) << (8 * j);
-            else hi |= ((uint32_t)q & 0xffu) << (8 * (j - 4));
-        }
+        for (int j = 0; j < 8; ++j) b[j] = __float_as_uint(keep_f32(y[i][j] * mul) + 12582912.0f);
+        // low bytes of b0..b3 and b4..b7, gathered by byte permutes
+        const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u),
+                                                  0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
+                                                  0x05040100u);
         *reinterpret_cast<uint2 *>(qrow + c * 8) = make_uint2(lo, hi);
     }
     if (lane == 0) *pts2_row = scale2;

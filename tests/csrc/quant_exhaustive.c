@@ -13,10 +13,18 @@
  * over every finite fp16 row maximum amax > 0 and every fp16 x with
  * |x| <= amax (both signs), and counts the pairs whose int8 codes differ.
  * It prints "pairs <n> mismatches <m>" and exits non-zero if m > 0.
+ *
+ * Second check, for SwiGLU's re-quantisation (section 4 of the page,
+ * q = CAST_RINT(y * (127 / max|y|))): the GPU kernel rounds the fp32 product p
+ * to an integer by adding 1.5 * 2^23 and takes the low byte of the sum's bits
+ * as the int8 code.  For every float p with |p| <= 128 (every product that
+ * |y| <= max|y| allows, and more) this is compared with rintf(p) as an int8.
+ * It prints "rint values <n> mismatches <m>".
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <string.h>
 
 /* fp16 bit pattern (finite) -> float, from the definition of binary16 */
 static float half_to_float(uint16_t h) {
@@ -51,5 +59,24 @@ int main(void) {
         }
     }
     printf("pairs %lld mismatches %lld\n", pairs, bad);
-    return bad != 0;
+
+    long long vals = 0, bad2 = 0;
+    const uint32_t top = 0x43000000u; /* 128.0f */
+#pragma omp parallel for schedule(static) reduction(+ : vals, bad2)
+    for (long long u = 0; u <= (long long)top; ++u) {
+        for (int sgn = 0; sgn < 2; ++sgn) {
+            const uint32_t bits = (uint32_t)u | ((uint32_t)sgn << 31);
+            float p;
+            memcpy(&p, &bits, 4);
+            const float sum = p + 12582912.0f;
+            uint32_t sb;
+            memcpy(&sb, &sum, 4);
+            const int8_t got = (int8_t)(sb & 0xffu);
+            const int8_t ref = (int8_t)(int)rintf(p);
+            vals += 1;
+            bad2 += got != ref;
+        }
+    }
+    printf("rint values %lld mismatches %lld\n", vals, bad2);
+    return bad != 0 || bad2 != 0;
 }

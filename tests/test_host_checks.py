@@ -3,7 +3,9 @@
 * The quantiser's division (FrontReorder step 2c: q = CAST_ROUND(x / scale)):
   the FMA-corrected reciprocal form the GPU kernel uses gives the same int8
   code as rounding the IEEE quotient for every finite fp16 row maximum and
-  every fp16 value up to it (tests/csrc/quant_exhaustive.c).
+  every fp16 value up to it, and SwiGLU's rounding of the re-quantised product
+  by adding 1.5 * 2^23 equals rintf for every float up to 128 in magnitude
+  (tests/csrc/quant_exhaustive.c).
 * The C oracle built with AddressSanitizer and UndefinedBehaviorSanitizer runs
   clean on small shapes with dropped routes, zero rows, E = 1 and top_k = E
   (tests/csrc/oracle_asan_main.c).
@@ -40,6 +42,8 @@ def test_quantiser_division_exhaustive(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     words = r.stdout.split()
     assert words[0] == "pairs" and int(words[1]) > 10 ** 9 and words[3] == "0"
+    # SwiGLU's CAST_RINT by adding 1.5 * 2^23: every float with |p| <= 128
+    assert words[4:6] == ["rint", "values"] and int(words[6]) > 2 * 10 ** 9 and words[8] == "0"
 
 
 def test_oracle_under_sanitizers(tmp_path):
