@@ -8,10 +8,12 @@ The build also guards the grouped GEMM's register budget.  Its K loop issues
 the global -> LDS copies from inline assembly, which the compiler's wait-count
 pass does not see; any compiler-visible vector load that lands in the loop (a
 spill reload, for instance) gets a wait that in hardware also waits for every
-copy in flight and drains the copy ring.  The build therefore compiles the
-GEMM to assembly as well and fails if any scratch (spill) access lies inside
-a loop that issues those copies, or if an instantiation uses more registers
-or spills more values than recorded in GEMM_RESOURCES below.
+copy in flight and drains the copy ring.  The next tile's first copies are
+issued before the current tile's epilogue, so copies are in flight almost
+everywhere.  The build therefore compiles the GEMM to assembly as well and
+fails if the kernel accesses scratch (spill) memory anywhere, or if an
+instantiation uses more registers or spills more values than recorded in
+GEMM_RESOURCES below.
 """
 from __future__ import annotations
 
@@ -44,13 +46,15 @@ RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
 
 # Registers of each GEMM tile configuration, keyed by its template arguments
 # (BM, WAVES_M, WAVES_N, NS, TRIM, SKIP, PRIO, NTB): (VGPRs, AGPRs, spilled
-# values).  The 256-row tiles run 16 waves per CU, so 128 registers per wave
-# is the ceiling; their few spilled values are tile set-up values stored
-# before a tile's copies and reloaded after its K loop (checked below).
+# vector values, spilled scalar values).  The 256-row tiles run 16 waves per
+# CU, so 128 registers per wave is the ceiling.  Spilled scalar values go to
+# lanes of a vector register (v_writelane / v_readlane), not to memory; a
+# spilled vector value would go to scratch memory, which the checks below
+# forbid anywhere in the kernel.
 GEMM_RESOURCES = {
-    (64, 1, 4, 3, 1, 1, 16, 1): (110, 92, 0),
-    (256, 4, 4, 4, 0, 1, 0, 0): (128, 0, 6),
-    (256, 4, 4, 4, 0, 1, 0, 1): (128, 0, 6),
+    (64, 1, 4, 3, 1, 1, 16, 1): (110, 92, 0, 7),
+    (256, 4, 4, 4, 0, 1, 0, 0): (128, 0, 0, 13),
+    (256, 4, 4, 4, 0, 1, 0, 1): (128, 0, 0, 13),
 }
 GEMM_SRC = os.path.join(CSRC, "gmm.hip")
 
@@ -97,27 +101,32 @@ def check_gemm_resources(remarks: str) -> list[str]:
         if key is None:
             continue
         found += 1
-        got = (r.get("VGPRs", 0), r.get("AGPRs", 0),
-               r.get("VGPRs Spill", 0) + r.get("SGPRs Spill", 0))
+        got = (r.get("VGPRs", 0), r.get("AGPRs", 0), r.get("VGPRs Spill", 0),
+               r.get("SGPRs Spill", 0))
         rec = GEMM_RESOURCES.get(key)
+        desc = "VGPRs {}, AGPRs {}, vector spills {}, scalar spills {}"
         if rec is None:
-            problems.append(f"GEMM {key}: no record (VGPRs {got[0]}, AGPRs {got[1]}, "
-                            f"spills {got[2]})")
+            problems.append(f"GEMM {key}: no record ({desc.format(*got)})")
         elif any(g > r_ for g, r_ in zip(got, rec)):
-            problems.append(f"GEMM {key}: VGPRs {got[0]}, AGPRs {got[1]}, spills {got[2]} "
-                            f"above the record {rec[0]}, {rec[1]}, {rec[2]}")
+            problems.append(f"GEMM {key}: {desc.format(*got)} above the record "
+                            f"{desc.format(*rec)}")
     if not found:
         problems.append("no GEMM kernel found in the resource report")
     return problems
 
 
 def check_gemm_loops(asm: str) -> list[str]:
-    """No scratch access inside a loop that issues global -> LDS copies.
+    """No scratch access in a GEMM kernel, and none inside a copy loop.
 
-    The device assembly marks each basic block with its loop depth.  The
-    GEMM's tile loop is depth 1 and its K loops, nested in it, are depth 2 or
-    more; every run of nested blocks that contains a copy
-    (global_load_lds_dwordx4) must contain no scratch_ instruction."""
+    The ring copies (global_load_lds_dwordx4) are in flight through almost
+    the whole kernel: the next tile's first copies are issued before the
+    current tile's epilogue.  A scratch load (a spill reload) anywhere after
+    them gets a vmcnt wait that also waits for every copy and store issued
+    before it, so no GEMM kernel may access scratch memory at all.  The
+    device assembly also marks each basic block with its loop depth; the run
+    of nested blocks (depth 2 or more: the K loops inside the tile loop) that
+    contains a copy is reported separately, as that is where a reload would
+    drain the ring at every K step."""
     problems = []
     found = 0
     for func in asm.split("; -- Begin function ")[1:]:
@@ -125,6 +134,7 @@ def check_gemm_loops(asm: str) -> list[str]:
         if "gmm_i8_ring_kernel" not in name:
             continue
         found += 1
+        body = func.split(".Lfunc_end", 1)[0]
         depth, region = 0, []
 
         def close():
@@ -133,7 +143,7 @@ def check_gemm_loops(asm: str) -> list[str]:
                 problems.append(f"GEMM {gemm_template_args(name)}: a spill access inside a "
                                 "loop that issues the ring copies")
 
-        for line in func.split(".Lfunc_end", 1)[0].splitlines():
+        for line in body.splitlines():
             d = None
             m = re.search(r"Depth=(\d+)", line)
             if line.startswith(".LBB") or (m and "Loop Header" in line):
@@ -146,6 +156,9 @@ def check_gemm_loops(asm: str) -> list[str]:
             if depth >= 2:
                 region.append(line)
         close()
+        if re.search(r"^\s*scratch_", body, re.M):
+            problems.append(f"GEMM {gemm_template_args(name)}: scratch (spill) accesses "
+                            "in the kernel")
     if not found:
         problems.append("no GEMM kernel found in the assembly")
     return problems

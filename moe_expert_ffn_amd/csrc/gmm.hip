@@ -402,51 +402,98 @@ __device__ __forceinline__ void gmm_tail(const TailArgs &p, bool has_last_tile,
     }
 }
 
-// The epilogue through LDS.  Written straight from the MFMA layout, each
-// store instruction covers 32 bytes of 16 rows, so every 128-byte line of
-// the output took four partial writes.  Vector memory operations complete in
-// issue order, so the next tile's first copies waited for all of them (a
-// timing-only build without the stores ran GMM2 at large 27% faster).  Here
-// the waves first write the dequantised fp16 tile into the ring (free after
-// the K loop), rows of BN fp16 with 16-byte chunk c of row r at chunk
-// c ^ (r & 31), which keeps both the 8-byte writes of 16 rows and the
-// 16-byte reads along a row free of bank conflicts; then every wave stores
-// two whole rows per instruction (1 KB, full lines).  Rows [r_lo, r_hi) of
-// the tile are stored; live: this wave's accumulators hold tile rows.
-template <int TM, int TN, int NW>
-__device__ __forceinline__ void store_tile_coalesced(const GmmParams &p, const v4i (&acc)[TM][TN],
-                                                     const float *s_sc, int row0, int n0,
-                                                     int wm0, int wn0, int lane, int wave,
-                                                     int8_t *buf, int r_lo, int r_hi, bool live) {
-    constexpr int RB = kPackRows * 2;  // bytes of one tile row
-    __syncthreads();                   // every wave is done with the ring
-    if (live) {
+// The lane index, computed afresh where it is used.  In the 256-row kernel
+// every vector register is taken in the K loop, so a lane value kept from
+// before it would be spilled, and its reload (a vector memory load) would
+// wait for every copy and store issued before it.
+__device__ __forceinline__ int fresh_lane_id() {
+    int l;
+    asm volatile(
+        "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+        "v_mbcnt_hi_u32_b32 %0, -1, %0"
+        : "=v"(l));
+    return l;
+}
+
+// The tile's output, dequantised to fp16 (fp32(acc) * scale, rounded to
+// fp32, then to fp16), stored in whole 128-byte lines without the ring and
+// without a workgroup barrier.  Each wave passes its 64 x 64 sub-tile through
+// its own 1 KB of LDS, 8 rows at a time: the 32 lanes that hold a chunk's 8
+// rows in the MFMA layout write them there (16-byte piece c of row rr at
+// slot c ^ rr, free of bank conflicts for both the 8-byte writes and the
+// row reads), then every lane reads one 16-byte piece of one row and the
+// wave stores 8 whole rows with one instruction.  A wave's LDS operations
+// complete in order, so no wait is needed between a chunk's writes and reads.
+// Since the ring is not used, the next tile's first copies can be in flight
+// while these stores go out.  Returns the number of store instructions
+// issued (wave-uniform).
+template <int TM, int TN>
+__device__ __forceinline__ int store_tile_private(const GmmParams &p, const v4i (&acc)[TM][TN],
+                                                  const float *s_sc, int row0, int n0, int wm0,
+                                                  int wn0, int8_t *wbuf, int r_lo, int r_hi,
+                                                  bool live) {
+    static_assert(TN == 4, "a wave's sub-tile row is 64 columns, one 128-byte line of fp16");
+    // N is a multiple of 128, so a sub-tile's columns are all inside N or all past it
+    if (!live || n0 + wn0 >= p.N) return 0;
+    const int lane = fresh_lane_id();
+    int nstores = 0;
+    // rows 16 i .. 16 i + 15 of the sub-tile: chunks 2 i and 2 i + 1
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int rb0 = wm0 + 16 * i;  // tile row of the first row
+        if (rb0 + 16 <= r_lo || rb0 >= r_hi) continue;  // no output row in these chunks
+        uint2 h[TN];  // fp16 of the lane's values of row 16 i + (lane & 15), two per word
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int cl = wn0 + 16 * j + 4 * (lane >> 4);
-            const float4 s4 = *reinterpret_cast<const float4 *>(s_sc + cl);
-            const float s[4] = {s4.x, s4.y, s4.z, s4.w};
-            const int chunk = cl >> 3, half = (cl >> 2) & 1;
+            const float4 s4 =
+                *reinterpret_cast<const float4 *>(s_sc + wn0 + 16 * j + 4 * (lane >> 4));
+            const uint32_t h0 = f2h(keep_f32((float)acc[i][j][0] * s4.x));
+            const uint32_t h1 = f2h(keep_f32((float)acc[i][j][1] * s4.y));
+            const uint32_t h2 = f2h(keep_f32((float)acc[i][j][2] * s4.z));
+            const uint32_t h3 = f2h(keep_f32((float)acc[i][j][3] * s4.w));
+            h[j] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        }
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int rl = wm0 + 16 * i + (lane & 15);
-                uint32_t h[4];
+        for (int half = 0; half < 2; ++half) {
+            const int rb = rb0 + 8 * half;  // tile row of the chunk's first row
+            if (rb + 8 <= r_lo || rb >= r_hi) continue;
+            // lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3
+            if (((lane >> 3) & 1) == half) {
+                const int rr = lane & 7;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) h[v] = f2h(keep_f32((float)acc[i][j][v] * s[v]));
-                *reinterpret_cast<uint2 *>(buf + rl * RB + ((chunk ^ (rl & 31)) << 4) +
-                                           (half << 3)) =
-                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                for (int j = 0; j < TN; ++j) {
+                    const int c = 2 * j + (lane >> 5);  // 16-byte piece of the row
+                    *reinterpret_cast<uint2 *>(wbuf + rr * 128 + ((c ^ rr) << 4) +
+                                               (((lane >> 4) & 1) << 3)) = h[j];
+                }
             }
+            const int rr = lane >> 3, c = lane & 7;
+            const uint4 v = *reinterpret_cast<const uint4 *>(wbuf + rr * 128 + ((c ^ rr) << 4));
+            const int r = rb + rr;
+            // at least one row of the chunk is stored, so the instruction issues
+            if (r >= r_lo && r < r_hi)
+                store_nt16(p.C + (size_t)(row0 + r) * p.N + n0 + wn0 + 8 * c, v);
+            ++nstores;
         }
     }
-    __syncthreads();
-    const int c = lane & 31;  // 16-byte chunk of a row: columns 8 c .. 8 c + 7
-    const bool col_ok = n0 + 8 * c < p.N;  // N is a multiple of 128
-    for (int r = r_lo + 2 * wave + (lane >> 5); r < r_hi; r += 2 * NW) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(buf + r * RB + ((c ^ (r & 31)) << 4));
-        if (col_ok) store_nt16(p.C + (size_t)(row0 + r) * p.N + n0 + 8 * c, v);
+    return nstores;
+}
+
+// s_waitcnt vmcnt(base + extra) for a wave-uniform extra in [0, 8]
+template <int base>
+__device__ __forceinline__ void wait_vmcnt_plus(int extra) {
+    switch (extra) {
+        case 0: wait_vmcnt<base>(); break;
+        case 1: wait_vmcnt<base + 1>(); break;
+        case 2: wait_vmcnt<base + 2>(); break;
+        case 3: wait_vmcnt<base + 3>(); break;
+        case 4: wait_vmcnt<base + 4>(); break;
+        case 5: wait_vmcnt<base + 5>(); break;
+        case 6: wait_vmcnt<base + 6>(); break;
+        case 7: wait_vmcnt<base + 7>(); break;
+        case 8: wait_vmcnt<base + 8>(); break;
+        default: wait_vmcnt<0>(); break;
     }
-    __syncthreads();  // the ring is free again for the next tile's copies
 }
 
 template <int BM, int WAVES_M, int WAVES_N, int NS, bool TRIM, bool SKIP = true, int PRIO = 0,
@@ -484,6 +531,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     // stored, row piece): kept in LDS by tile parity, not in registers
     // across the K loop, which uses every scalar register
     __shared__ int s_tile[2][6];
+    __shared__ __attribute__((aligned(16))) int8_t s_wbuf[NW][1024];  // epilogue, per wave
 
     // the wave index is uniform: kept in a scalar register, so that no
     // vector register holds threadIdx across the K loop
@@ -638,26 +686,41 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         return ts;
     };
 
+    // the copies of K slice `stage` of tile t into its ring slot
+    auto issue = [&](const TileSetup &t, int stage) {
+        if (stage >= nst) return;
+        const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
+        const int8_t *abase = p.A + (size_t)stage * kBK64;
+        const int8_t *bbase = t.btile + (size_t)stage * bstep;
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const uint32_t dst =
+                __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024));
+            // weights that are read by one tile only (NTB) carry the non-temporal hint
+            if (j < kAJ) dma16(abase, t.voff[j], dst);
+            else if (NTB) dma16_nt(bbase, t.voff[j], dst);
+            else dma16(bbase, t.voff[j], dst);
+        }
+    };
+    // A tile's first NS stages fill the ring; its K loop starts once stage 0
+    // has landed (stages 1 .. NS - 1 may still be in flight).  The first tile
+    // issues them here, every later one between the previous tile's K loop
+    // and its epilogue.
+    auto issue_first = [&](const TileSetup &t) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) issue(t, st);
+    };
+
     int parity = 0;
     TileSetup cur = setup(0, 0);
+    if (cur.valid) {
+        issue_first(cur);
+        if (nst >= NS) wait_vmcnt<(NS - 1) * LPW>();
+        else wait_vmcnt<0>();
+    }
     for (int k = 0; cur.valid; ++k, parity ^= 1) {
         const int rows = cur.rows;
         const bool piece_tile = cur.piece_tile;
-        auto issue = [&](int stage) {
-            if (stage >= nst) return;
-            const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
-            const int8_t *abase = p.A + (size_t)stage * kBK64;
-            const int8_t *bbase = cur.btile + (size_t)stage * bstep;
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) {
-                const uint32_t dst =
-                    __builtin_amdgcn_readfirstlane(sbase + (uint32_t)((wave + j * NW) * 1024));
-                // weights that are read by one tile only (NTB) carry the non-temporal hint
-                if (j < kAJ) dma16(abase, cur.voff[j], dst);
-                else if (NTB) dma16_nt(bbase, cur.voff[j], dst);
-                else dma16(bbase, cur.voff[j], dst);
-            }
-        };
 
         v4i acc[TM][TN];
 #pragma unroll
@@ -689,26 +752,23 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 }
             };
             // stage kt+1 must have landed; stages up to kt+NS-1 were issued,
-            // the NS-2 after kt+1 may be in flight
+            // the NS-2 after kt+1 may be in flight (the previous tile's
+            // epilogue stores are older than stage 1, so they are done too)
             auto await_next = [&](int kt) {
                 if (kt + NS - 1 < nst) wait_vmcnt<(NS - 2) * LPW>();
                 else wait_vmcnt<0>();
                 __syncthreads();
             };
-#pragma unroll
-            for (int st = 0; st < NS; ++st) issue(st);
-            if (nst >= NS) wait_vmcnt<(NS - 1) * LPW>();
-            else wait_vmcnt<0>();
-            __syncthreads();
+            __syncthreads();  // publishes stage 0 (awaited by every wave)
             frag(0, fa[0], fb[0]);
 
             // two stages per trip so that the register set of every stage is
             // known at compile time (set = stage & 1); nst is even
             for (int kt0 = 0; kt0 < nst; kt0 += 2) {
                 static_for<0, 2>([&](auto uc) {
-                    constexpr int cur = decltype(uc)::value, nxt = cur ^ 1;
-                    const int kt = kt0 + cur;
-                    if constexpr (PRIO > 0 && cur == 0) {
+                    constexpr int rs = decltype(uc)::value, rn = rs ^ 1;  // register sets
+                    const int kt = kt0 + rs;
+                    if constexpr (PRIO > 0 && rs == 0) {
                         static_assert(PRIO % 2 == 0, "kt is even here");
                         if (kt % PRIO == 0) {
                             if (((kt / PRIO) & 1) ^ late) __builtin_amdgcn_s_setprio(2);
@@ -716,9 +776,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                         }
                     }
                     await_next(kt);
-                    issue(kt + NS);
-                    frag(kt + 1, fa[nxt], fb[nxt]);
-                    mfmas(fa[cur], fb[cur]);
+                    issue(cur, kt + NS);
+                    frag(kt + 1, fa[rn], fb[rn]);
+                    mfmas(fa[rs], fb[rs]);
                 });
             }
         };
@@ -730,23 +790,31 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
 
         // the next tile's set-up (its scale copy goes to the other LDS slot)
         const TileSetup nxt = setup(k + 1, parity ^ 1);
-        // every copy of the tile has been awaited inside the loop (the scale
-        // copy is older than all of them), and the last barrier published them.
-        // The int32 accumulators of the debug output go straight from the
-        // registers, and the fp16 tile with them.
-        static_assert(BM * kPackRows * 2 <= NS * kStage, "the fp16 tile fits in the ring");
-        {
-            const int t_row0 = __builtin_amdgcn_readfirstlane(s_tile[parity][0]);
-            const int t_rows = __builtin_amdgcn_readfirstlane(s_tile[parity][1]);
-            const int t_n0 = __builtin_amdgcn_readfirstlane(s_tile[parity][2]);
-            const int r_lo = __builtin_amdgcn_readfirstlane(s_tile[parity][3]);
-            const int r_hi = __builtin_amdgcn_readfirstlane(s_tile[parity][4]);
-            const bool t_piece = __builtin_amdgcn_readfirstlane(s_tile[parity][5]) != 0;
-            const bool live = (!t_piece || wave / WAVES_N == piece) && wm0 < t_rows;
-            if (p.acc_dbg && live)
-                store_acc_dbg<TM, TN>(p, acc, t_row0, t_rows, t_n0, wm0, wn0, lane);
-            store_tile_coalesced<TM, TN, NW>(p, acc, s_scale[parity], t_row0, t_n0, wm0, wn0, lane,
-                                             wave, smem, r_lo, r_hi, live);
+        const int t_row0 = __builtin_amdgcn_readfirstlane(s_tile[parity][0]);
+        const int t_rows = __builtin_amdgcn_readfirstlane(s_tile[parity][1]);
+        const int t_n0 = __builtin_amdgcn_readfirstlane(s_tile[parity][2]);
+        const int r_lo = __builtin_amdgcn_readfirstlane(s_tile[parity][3]);
+        const int r_hi = __builtin_amdgcn_readfirstlane(s_tile[parity][4]);
+        const bool t_piece = __builtin_amdgcn_readfirstlane(s_tile[parity][5]) != 0;
+        const bool live = (!t_piece || wave / WAVES_N == piece) && wm0 < t_rows;
+        // the debug int32 accumulators go straight from the registers, before
+        // the next tile's copies, so the wait for its first stage covers them
+        if (p.acc_dbg && live) store_acc_dbg<TM, TN>(p, acc, t_row0, t_rows, t_n0, wm0, wn0, lane);
+        // The next tile's stage 0 is copied while this tile's output is stored,
+        // and its stages 1 .. NS - 1 after the stores: vector memory
+        // operations complete in issue order, so the K loop's waits for
+        // stages 1 and later then cover the stores without counting them,
+        // and only the wait for stage 0 allows for them.
+        __syncthreads();  // every wave has read its last fragments: the ring is free
+        if (nxt.valid) issue(nxt, 0);
+        const int nstores = store_tile_private<TM, TN>(p, acc, s_scale[parity], t_row0, t_n0, wm0,
+                                                       wn0, s_wbuf[wave], r_lo, r_hi, live);
+        if (nxt.valid) {
+#pragma unroll
+            for (int st = 1; st < NS; ++st) issue(nxt, st);
+            // stage 0 (and the tile's older scale copy) has landed
+            if (nst >= NS) wait_vmcnt_plus<(NS - 1) * LPW>(nstores);
+            else wait_vmcnt<0>();
         }
         if constexpr (!TRIM) {
             // done with round F - 2: count this workgroup for the last-round SwiGLU

@@ -10,7 +10,8 @@
   clean on small shapes with dropped routes, zero rows, E = 1 and top_k = E
   (tests/csrc/oracle_asan_main.c).
 * The grouped GEMM's register guard: the compiler's resource report of every
-  GEMM instantiation shows no spills and no more registers than recorded.
+  GEMM instantiation shows no more registers or spilled values than recorded,
+  and its assembly has no scratch (spill) access at all.
 """
 from __future__ import annotations
 
@@ -89,27 +90,31 @@ def test_gemm_register_guard_rejects_spills_and_growth():
     assert any("above the record" in p for p in problems)
 
 
-def _fake_asm(reload_in_loop: bool) -> str:
+def _fake_asm(reload: str) -> str:
     """A GEMM function in the compiler's assembly layout: a tile loop (depth
-    1) holding a K loop (depth 2) that issues a copy; one spill reload either
-    inside the K loop or after it."""
-    reload = "\tscratch_load_dword v0, off, off offset:8 ; 4-byte Folded Reload\n"
+    1) holding a K loop (depth 2) that issues a copy; one spill reload inside
+    the K loop ("loop"), after it ("after"), or none ("none")."""
+    rl = "\tscratch_load_dword v0, off, off offset:8 ; 4-byte Folded Reload\n"
     return (f"; -- Begin function {_GEMM_NAME}\n"
             ".LBB2_48:                ; =>This Loop Header: Depth=1\n"
             "\tv_mov_b32 v1, 0\n"
             ".LBB2_85:                ;   Parent Loop BB2_48 Depth=1\n"
             "                         ; =>  This Inner Loop Header: Depth=2\n"
             "\tglobal_load_lds_dwordx4 v2, s[4:5]\n"
-            + (reload if reload_in_loop else "") +
+            + (rl if reload == "loop" else "") +
             "\tv_mfma_i32_16x16x64_i8 v[0:3], v[4:7], v[8:11], v[0:3]\n"
             "\ts_cbranch_scc1 .LBB2_85\n"
             ".LBB2_97:                ;   in Loop: Header=BB2_48 Depth=1\n"
-            + ("" if reload_in_loop else reload) +
+            + (rl if reload == "after" else "") +
             "\ts_cbranch_scc1 .LBB2_48\n"
             ".Lfunc_end2:\n")
 
 
-def test_gemm_loop_guard_rejects_a_reload_in_the_copy_loop():
-    assert B.check_gemm_loops(_fake_asm(reload_in_loop=False)) == []
-    problems = B.check_gemm_loops(_fake_asm(reload_in_loop=True))
-    assert problems and "inside a loop" in problems[0]
+def test_gemm_loop_guard_rejects_any_reload():
+    # the next tile's copies are in flight through the epilogue, so a reload
+    # after the K loop is rejected as well as one inside it
+    assert B.check_gemm_loops(_fake_asm("none")) == []
+    after = B.check_gemm_loops(_fake_asm("after"))
+    assert len(after) == 1 and "scratch" in after[0]
+    inside = B.check_gemm_loops(_fake_asm("loop"))
+    assert any("inside a loop" in p for p in inside) and any("scratch" in p for p in inside)
