@@ -58,10 +58,14 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
             const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[u]);
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
-                const float g0 = h2f((uint16_t)(w[j >> 1] & 0xffffu));
-                const float g1 = h2f((uint16_t)(w[j >> 1] >> 16));
+                // fp32(g) * scale as an FMA with a +0 addend, so that the
+                // hardware reads the fp16 value in the same instruction: the
+                // same rounded product, except that -0 becomes +0, and the sum
+                // below starts at +0, so that changes no result
+                const float g0 = __builtin_fmaf(h2f((uint16_t)(w[j >> 1] & 0xffffu)), sc[u], 0.0f);
+                const float g1 = __builtin_fmaf(h2f((uint16_t)(w[j >> 1] >> 16)), sc[u], 0.0f);
                 // combine: cast the dequantised row to the output type
-                const uint32_t deq = f2bf_pk(g0 * sc[u], g1 * sc[u]);
+                const uint32_t deq = f2bf_pk(g0, g1);
                 acc[j] = acc[j] + bf2f_lo(deq) * p[u];
                 acc[j + 1] = acc[j + 1] + bf2f_hi(deq) * p[u];
             }
