@@ -64,13 +64,17 @@ __device__ __forceinline__ void static_for(F &&f) {
 // weight block stay adjacent.  s_pre[c - 1][e] counts the tiles of class c of
 // the experts before e (s_pre[c - 1][E]: all of class c).  With U = 1 this is
 // the plain expert / n-block / m-block order.
+//
+// s_pad (nullable): s_pad[e] = the experts before e with an odd row count,
+// the offset of expert e's rows in the row-paired layout of A (a_pair).
 template <int BM, int UNIT>
 __device__ __forceinline__ int build_schedule(const GmmParams &p, int NB, int (*s_pre)[kMaxE + 1],
-                                              int *s_row_off, int *s_rows) {
+                                              int *s_row_off, int *s_rows, int *s_pad = nullptr) {
     constexpr int U = BM / UNIT;
     const int lane = threadIdx.x & (kWave - 1);
     if ((threadIdx.x >> 6) == 0) {
         int run[U];
+        int odd_run = 0;
 #pragma unroll
         for (int c = 0; c < U; ++c) run[c] = 0;
         for (int base = 0; base < p.E; base += kWave) {
@@ -95,6 +99,12 @@ __device__ __forceinline__ int build_schedule(const GmmParams &p, int NB, int (*
             if (e < p.E) {
                 s_row_off[e] = off;
                 s_rows[e] = rows;
+            }
+            if (s_pad) {
+                const int odd = rows & 1;
+                const int incl = wave_inclusive_scan(odd);
+                if (e < p.E) s_pad[e] = odd_run + incl - odd;
+                odd_run += __shfl(incl, kWave - 1, kWave);
             }
         }
         if (lane == 0) {
@@ -292,6 +302,7 @@ struct TailArgs {
     const float *pts1;
     uint32_t *sync;     // [3]: arrivals, row chunks taken, last-round workgroups done
     uint8_t *done;
+    const int32_t *prow;  // nullable: q2 row-paired, row r at paired row prow[r]
     int I, spin, E;
 };
 
@@ -396,7 +407,12 @@ __device__ __forceinline__ void gmm_tail(const TailArgs &p, bool has_last_tile,
             uint4 uraw[4], graw[4];  // I <= 2048: at most 4 chunks of 8 columns per lane
             swiglu_row_load<4>(p.C + (size_t)r * (2 * I), I, lane, uraw, graw);
             const float p1 = p.pts1[r];
-            swiglu_row_finish<4>(uraw, graw, p1, I, lane, p.q2 + (size_t)r * I, p.pts2 + r);
+            int8_t *qrow = p.q2 + (size_t)r * I;
+            if (p.prow) {
+                const int pr = p.prow[r];
+                qrow = p.q2 + (size_t)(pr >> 1) * (2 * I) + (pr & 1) * 64;
+            }
+            swiglu_row_finish<4>(uraw, graw, p1, I, lane, qrow, p.prow ? 128 : 64, p.pts2 + r);
             if (lane == 0) p.done[r] = 1;
         }
     }
@@ -524,6 +540,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     __shared__ int s_pre[U][kMaxE + 1];
     __shared__ int s_row_off[kMaxE];
     __shared__ int s_rows[kMaxE];
+    __shared__ int s_pad[kMaxE];  // row offsets in the row-paired A layout (a_pair)
     __shared__ int s_go;
     __shared__ TailArgs s_targs;  // last-round SwiGLU (GMM1 only)
     __shared__ int s_tail_round;  // the round after which producers count themselves, or -1
@@ -539,7 +556,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     const int lane = __lane_id();
     const int N = p.N, Kred = p.Kred;
     const int NB = (N + BN - 1) / BN;
-    const int total = build_schedule<BM, BM / WAVES_M>(p, NB, s_pre, s_row_off, s_rows);
+    const int total =
+        build_schedule<BM, BM / WAVES_M>(p, NB, s_pre, s_row_off, s_rows, p.a_pair ? s_pad : nullptr);
 
     // TRIM (active grid, for tiles of equal cost that stream weights): with
     // k = ceil(total / gridDim) tiles for the busiest workgroup, ceil(total / k)
@@ -614,7 +632,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             const bool on = p.tail_q2 != nullptr && F >= 2 && L > 0 && p.tail_I <= 2048;
             s_tail_round = on ? F - 1 : -1;
             s_targs = TailArgs{p.C, p.tail_q2, p.tail_pts2, p.tail_pts1, p.tail_sync,
-                               p.tail_done, p.tail_I, p.tail_spin, p.E};
+                               p.tail_done, p.tail_prow, p.tail_I, p.tail_spin, p.E};
         }
     }
 
@@ -675,8 +693,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
                 const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
                 const int arow =
                     tr.row0 + (ts.piece_tile ? min(max(r, plo), phi) : min(r, tr.rows - 1));
-                const int srow = p.a_route ? p.a_route[arow] / p.a_div : arow;
-                ts.voff[j] = (uint32_t)srow * (uint32_t)Kred + kc * 16;
+                if (p.a_pair) {  // padded row g: 64-byte K slices of rows 2m, 2m + 1 share a line
+                    const int g = arow + s_pad[tr.e];
+                    ts.voff[j] = (uint32_t)(g >> 1) * (uint32_t)(2 * Kred) + (g & 1) * 64 + kc * 16;
+                } else {
+                    const int srow = p.a_route ? p.a_route[arow] / p.a_div : arow;
+                    ts.voff[j] = (uint32_t)srow * (uint32_t)Kred + kc * 16;
+                }
             } else {
                 const int q = pch - BM * 4;
                 const int r = q >> 2, kc = (q & 3) ^ swz64(q >> 2);
@@ -686,11 +709,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         return ts;
     };
 
+    // bytes between the A operand's K slices of one row
+    const int a_stage = p.a_pair ? 2 * kBK64 : kBK64;
     // the copies of K slice `stage` of tile t into its ring slot
     auto issue = [&](const TileSetup &t, int stage) {
         if (stage >= nst) return;
         const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
-        const int8_t *abase = p.A + (size_t)stage * kBK64;
+        const int8_t *abase = p.A + (size_t)stage * a_stage;
         const int8_t *bbase = t.btile + (size_t)stage * bstep;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {

@@ -28,6 +28,12 @@ struct GmmParams {
     uint8_t *tail_done = nullptr;     // [R] set for each row the last round did
     int tail_I = 0;
     int tail_spin = 0;                // poll limit of the wait; < 0: give up at once
+    const int32_t *tail_prow = nullptr;  // nullable: q2 row-paired (see a_pair), row r at tail_prow[r]
+    // A in the row-paired layout (GEMMs without a_route): every expert's group
+    // is padded to an even row count, and padded rows 2m and 2m + 1 share each
+    // 128-byte line, [Rp / 2][Kred / 64][2][64] bytes.  A copy instruction of
+    // the K loop then reads 8 whole lines instead of 16 half lines.
+    int a_pair = 0;
 };
 
 // block_counts: device scratch of route_sort_workspace_bytes(R, E) bytes
@@ -36,6 +42,9 @@ hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *s
                              int32_t *expanded_row_idx, int32_t *tokens_per_expert,
                              int32_t *expert_cumsum, int32_t *err_word, int32_t *block_counts,
                              hipStream_t stream);
+// prow (nullable, forward only): prow[row] = row + the number of experts before
+// the row's expert with an odd row count, the row's place in the row-paired
+// layout of q2 (see GmmParams::a_pair), written with the sort.
 // Route sort and quant scatter in one launch, for R <= 8192 and top_k <= 16
 // (permute_fused_ok); same outputs as launch_route_sort + launch_quant_scatter.
 bool permute_fused_ok(int R, int top_k);
@@ -46,7 +55,7 @@ hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, in
                                 int32_t *sorted_route, int32_t *tokens_per_expert,
                                 int32_t *expert_cumsum, int32_t *err_word, bool token_major,
                                 hipStream_t stream, uint8_t *tail_done = nullptr,
-                                uint32_t *tail_sync = nullptr);
+                                uint32_t *tail_sync = nullptr, int32_t *prow = nullptr);
 // The forward's permute for route counts beyond the one-launch path: the
 // route counts and the token-major quantisation in one launch (per-token
 // scales to tscale [M]), then the scatter pass, which also writes pts1.
@@ -56,13 +65,16 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
                                        int32_t *tokens_per_expert, int32_t *expert_cumsum,
                                        int32_t *err_word, int32_t *block_counts, float *tscale,
                                        hipStream_t stream, uint8_t *tail_done = nullptr,
-                                       uint32_t *tail_sync = nullptr);
+                                       uint32_t *tail_sync = nullptr, int32_t *prow = nullptr);
 hipError_t launch_quant_scatter(const uint16_t *x, const int32_t *expanded_row_idx, int M, int K,
                                 int top_k, int8_t *gmA, float *pts1, bool token_major,
                                 hipStream_t stream);
+// prow (nullable): q2 in the row-paired layout, row r at paired row prow[r]
+// (see GmmParams::a_pair); else q2 is [R, I] row-major.
 hipError_t launch_swiglu_quant(const uint16_t *gmC, const float *pts1,
                                const int32_t *expert_cumsum, int R, int E, int I, int8_t *q2,
-                               float *pts2, hipStream_t stream, const uint8_t *skip = nullptr);
+                               float *pts2, hipStream_t stream, const uint8_t *skip = nullptr,
+                               const int32_t *prow = nullptr);
 hipError_t launch_unpermute(const uint16_t *gmm2_out, const float *pts2,
                             const int32_t *expanded_row_idx, const float *probs, int M, int K,
                             int top_k, uint16_t *out, hipStream_t stream);

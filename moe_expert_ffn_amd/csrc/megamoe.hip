@@ -73,8 +73,8 @@ int32_t *scratch_device_ptr() {
 }
 
 struct Layout {
-    size_t err, bcnt, tscale, tsync, tdone, eri, sorted, counts, cumsum, pts1, pts2, gmA, gmC, q2,
-        g2, total;
+    size_t err, bcnt, tscale, tsync, tdone, eri, sorted, counts, cumsum, pts1, pts2, prow, gmA,
+        gmC, q2, g2, total;
 };
 
 // permute workspace: error word, the sort's per-block expert counts, then the
@@ -99,10 +99,13 @@ Layout forward_layout(const megamoe_dims &d) {
     L.cumsum = o; o += align_up((size_t)d.E * 4);
     L.pts1 = o;   o += align_up(R * 4);
     L.pts2 = o;   o += align_up(R * 4);
+    L.prow = o;   o += align_up(R * 4);
     o = align_big(o);
     L.gmA = o;    o = align_big(o + (size_t)d.M * d.K);   // token-major quantised x
     L.gmC = o;    o = align_big(o + R * 2 * d.I * 2);
-    L.q2 = o;     o = align_big(o + R * d.I);
+    // q2, row-paired when GMM2 uses the 256-row tiles: each expert's rows are
+    // padded to an even count, at most R + E rows
+    L.q2 = o;     o = align_big(o + (R + d.E + 1) * d.I);
     L.g2 = o;     o += align_up(R * d.K * 2);
     L.total = o;
     return L;
@@ -126,17 +129,17 @@ int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_
                 float *pts1, int32_t *eri, int32_t *sorted, int32_t *counts, int32_t *cumsum,
                 int32_t *err_word, int32_t *block_counts, bool token_major, hipStream_t s,
                 float *tscale = nullptr, uint8_t *tail_done = nullptr,
-                uint32_t *tail_sync = nullptr) {
+                uint32_t *tail_sync = nullptr, int32_t *prow = nullptr) {
     const int R = d.M * d.top_k;
     if (permute_fused_ok(R, d.top_k))
         return hip_status(launch_permute_fused(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA, pts1, eri,
                                                sorted, counts, cumsum, err_word, token_major, s,
-                                               tail_done, tail_sync));
+                                               tail_done, tail_sync, prow));
     if (token_major && tscale)
         return hip_status(launch_permute_tokens_2pass(x, expert_idx, d.M, d.K, d.E, d.top_k, gmA,
                                                       pts1, eri, sorted, counts, cumsum, err_word,
                                                       block_counts, tscale, s, tail_done,
-                                                      tail_sync));
+                                                      tail_sync, prow));
     MEGAMOE_TRY(hip_status(launch_route_sort(expert_idx, R, d.E, sorted, eri, counts, cumsum,
                                              err_word, block_counts, s)));
     return hip_status(
@@ -145,11 +148,14 @@ int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_
 
 // a_route (nullable): A row d is token a_route[d] / top_k of a token-major A.
 // tail (nullable, GMM1 only): SwiGLU in GMM1's last round, see gmm.hip.
+// a_pair: A is in the row-paired layout (GmmParams::a_pair).
 int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const int8_t *Bp,
             const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s,
-            const int32_t *a_route = nullptr, const GmmParams *tail = nullptr) {
+            const int32_t *a_route = nullptr, const GmmParams *tail = nullptr,
+            bool a_pair = false) {
     const int R = d.M * d.top_k;
     GmmParams prm{A, Bp, scale, cumsum, C, dbg, d.E, N, Kred, a_route, d.top_k};
+    prm.a_pair = a_pair ? 1 : 0;
     if (tail) {
         prm.tail_q2 = tail->tail_q2;
         prm.tail_pts2 = tail->tail_pts2;
@@ -158,6 +164,7 @@ int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const
         prm.tail_done = tail->tail_done;
         prm.tail_I = tail->tail_I;
         prm.tail_spin = tail->tail_spin;
+        prm.tail_prow = tail->tail_prow;
     }
     return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
 }
@@ -373,12 +380,17 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     const int R = d->M * d->top_k;
     const int overlap = g_overlap.load(std::memory_order_relaxed);
     const bool tail = overlap != 0 && gmm_tail_ok(R, d->E, d->I);
+    // GMM2 with the 256-row tiles reads q2 in the row-paired layout: the
+    // 64-byte K slices of two rows share each 128-byte line, so its A copies
+    // read whole lines (the sort writes each row's paired place to prow)
+    const bool pair = gmm_pick_variant(R, d->E) != 0;
+    int32_t *prow = pair ? (int32_t *)(base + L.prow) : nullptr;
     // the quantised tokens are written once, token-major; GMM1 gathers its
     // expert-sorted rows from them through the route list, so the top_k
     // copies of each token are never written to or re-read from HBM
     MEGAMOE_TRY(run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, bcnt,
                             true, s, (float *)(base + L.tscale), tail ? tdone : nullptr,
-                            tail ? tsync : nullptr));
+                            tail ? tsync : nullptr, prow));
     // SwiGLU: the rows whose GMM1 output is complete before GMM1's last round
     // are done by the workgroups left idle in that round; the SwiGLU kernel
     // does the rest (all rows without the overlap)
@@ -390,11 +402,13 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     tp.tail_done = tdone;
     tp.tail_I = d->I;
     tp.tail_spin = overlap == 2 ? -1 : kTailSpin;
+    tp.tail_prow = prow;
     MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s, sorted,
                         tail ? &tp : nullptr));
     MEGAMOE_TRY(hip_status(launch_swiglu_quant(gmC, pts1, cumsum, R, d->E, d->I, q2, pts2, s,
-                                               tail ? tdone : nullptr)));
-    MEGAMOE_TRY(run_gmm(*d, q2, cumsum, w2p, scale2, g2, nullptr, d->K, d->I, s));
+                                               tail ? tdone : nullptr, prow)));
+    MEGAMOE_TRY(run_gmm(*d, q2, cumsum, w2p, scale2, g2, nullptr, d->K, d->I, s, nullptr, nullptr,
+                        pair));
     return hip_status(launch_unpermute(g2, pts2, eri, probs, d->M, d->K, d->top_k, out, s));
 }
 

@@ -164,9 +164,11 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
     int32_t *__restrict__ expanded_row_idx, int32_t *__restrict__ tokens_per_expert,
     int32_t *__restrict__ expert_cumsum, int32_t *__restrict__ err_word,
     const float *__restrict__ tscale, int top_k, float *__restrict__ pts1,
-    uint8_t *__restrict__ tail_done, uint32_t *__restrict__ tail_sync) {
+    uint8_t *__restrict__ tail_done, uint32_t *__restrict__ tail_sync,
+    int32_t *__restrict__ prow) {
     __shared__ int s_base[kMaxExperts];   // next row of each expert for this block
     __shared__ int s_tot[kMaxExperts];
+    __shared__ int s_odd[kMaxExperts];    // experts before e with an odd row count
     __shared__ int s_wcnt[kSortWavesB][kMaxExperts];
     __shared__ int s_valid;
 
@@ -224,6 +226,10 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
         }
         const int incl = wave_inclusive_scan(sum);
         int run = incl - sum;
+        int odds = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) odds += v[j] & 1;
+        int orun = wave_inclusive_scan(odds) - odds;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane * 4 + j;
@@ -233,8 +239,10 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
                     expert_cumsum[e] = run + v[j];
                 }
                 s_base[e] += run;
+                s_odd[e] = orun;
             }
             run += v[j];
+            orun += v[j] & 1;
         }
         if (lane == kWave - 1) s_valid = incl;
     }
@@ -276,6 +284,7 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
             if (dst >= 0) {
                 sorted_route[dst] = r;
                 if (tscale) pts1[dst] = ts;
+                if (prow) prow[dst] = dst + s_odd[key];
             }
         }
         __syncthreads();
@@ -409,7 +418,7 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     int32_t *__restrict__ expanded_row_idx, int32_t *__restrict__ sorted_route,
     int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_cumsum,
     int32_t *__restrict__ err_word, bool token_major, uint8_t *__restrict__ tail_done,
-    uint32_t *__restrict__ tail_sync) {
+    uint32_t *__restrict__ tail_sync, int32_t *__restrict__ prow) {
     __shared__ int h_all[kMaxExperts + 1];
     __shared__ int h_pre[kMaxExperts + 1];
     __shared__ int s_key[kFusedMaxTopK];
@@ -496,6 +505,10 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
         }
         const int incl = wave_inclusive_scan(sum);
         int run = incl - sum;
+        int odds = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) odds += v[j] & 1;
+        int orun = wave_inclusive_scan(odds) - odds;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = lane * 4 + j;
@@ -505,8 +518,10 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
                     expert_cumsum[e] = run + v[j];
                 }
                 h_pre[e] += run;  // first row of expert e for this token's routes
+                h_all[e] = orun;  // from here on: experts before e with an odd count
             }
             run += v[j];
+            orun += v[j] & 1;
         }
         if (lane == kWave - 1) s_valid = incl;
     }
@@ -524,6 +539,7 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
         if (dst >= 0) {
             sorted_route[dst] = r_own + tid;
             pts1[dst] = scale;
+            if (prow) prow[dst] = dst + h_all[key];
         }
     }
     if (t == 0) {
@@ -551,14 +567,15 @@ hipError_t launch_permute_fused(const uint16_t *x, const int32_t *expert_idx, in
                                 int top_k, int8_t *gmA, float *pts1, int32_t *expanded_row_idx,
                                 int32_t *sorted_route, int32_t *tokens_per_expert,
                                 int32_t *expert_cumsum, int32_t *err_word, bool token_major,
-                                hipStream_t stream, uint8_t *tail_done, uint32_t *tail_sync) {
+                                hipStream_t stream, uint8_t *tail_done, uint32_t *tail_sync,
+                                int32_t *prow) {
     const int R = M * top_k;
     const int per_thread = (K / 16 + 255) / 256;
     dim3 grid(M), block(256);
 #define MEGAMOE_PERMUTE_FUSED(C)                                                              \
     hipLaunchKernelGGL(permute_fused_kernel<C>, grid, block, 0, stream, x, expert_idx, R, E, K, \
                        top_k, gmA, pts1, expanded_row_idx, sorted_route, tokens_per_expert,     \
-                       expert_cumsum, err_word, token_major, tail_done, tail_sync)
+                       expert_cumsum, err_word, token_major, tail_done, tail_sync, prow)
     if (per_thread <= 1) MEGAMOE_PERMUTE_FUSED(1);
     else if (per_thread <= 2) MEGAMOE_PERMUTE_FUSED(2);
     else if (per_thread <= 4) MEGAMOE_PERMUTE_FUSED(4);
@@ -595,7 +612,7 @@ hipError_t launch_route_sort(const int32_t *expert_idx, int R, int E, int32_t *s
     hipLaunchKernelGGL(route_scatter_kernel, dim3(B), dim3(kSortBlock), 0, stream, expert_idx, R,
                        E, C, nbits, B, block_counts, sorted_route, expanded_row_idx,
                        tokens_per_expert, expert_cumsum, err_word, nullptr, 1, nullptr, nullptr,
-                       nullptr);
+                       nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -605,7 +622,7 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
                                        int32_t *tokens_per_expert, int32_t *expert_cumsum,
                                        int32_t *err_word, int32_t *block_counts, float *tscale,
                                        hipStream_t stream, uint8_t *tail_done,
-                                       uint32_t *tail_sync) {
+                                       uint32_t *tail_sync, int32_t *prow) {
     const int R = M * top_k;
     int nbits = 0;
     while ((1 << nbits) <= E) ++nbits;  // keys 0..E (E = dropped)
@@ -626,7 +643,7 @@ hipError_t launch_permute_tokens_2pass(const uint16_t *x, const int32_t *expert_
     hipLaunchKernelGGL(route_scatter_kernel, dim3(B), dim3(kSortBlock), 0, stream, expert_idx, R,
                        E, C, nbits, B, block_counts, sorted_route, expanded_row_idx,
                        tokens_per_expert, expert_cumsum, err_word, tscale, top_k, pts1, tail_done,
-                       tail_sync);
+                       tail_sync, prow);
     return hipGetLastError();
 }
 

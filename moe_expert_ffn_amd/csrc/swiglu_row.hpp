@@ -56,11 +56,13 @@ __device__ __forceinline__ void swiglu_row_load(const uint16_t *__restrict__ cro
 }
 
 // y, its row maximum, and the row's q2 codes and scale2 (p1: perTokenScale1).
+// The row's 64-byte K slices are stored slice_stride bytes apart from qrow
+// (64: a row-major row; 128: a row of the row-paired layout).
 template <int MAXC>
 __device__ __forceinline__ void swiglu_row_finish(const uint4 (&uraw)[MAXC],
                                                   const uint4 (&graw)[MAXC], float p1, int I,
                                                   int lane, int8_t *__restrict__ qrow,
-                                                  float *__restrict__ pts2_row) {
+                                                  int slice_stride, float *__restrict__ pts2_row) {
     const int nchunk = I >> 3;
     float y[MAXC][8];
     float amax = 0.0f;
@@ -109,7 +111,8 @@ __device__ __forceinline__ void swiglu_row_finish(const uint4 (&uraw)[MAXC],
         const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
                                                   __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
                                                   0x05040100u);
-        *reinterpret_cast<uint2 *>(qrow + c * 8) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2 *>(qrow + (c >> 3) * slice_stride + ((c & 7) << 3)) =
+            make_uint2(lo, hi);
     }
     if (lane == 0) *pts2_row = scale2;
 }

@@ -484,6 +484,10 @@ EDGES = {
     "rows_255_256_257_nt": ([255, 256, 257, 63, 64, 65, 100, 120], 512, 128),
     # 256-row tiles (mean > 256): one and two m-blocks
     "rows_255_256_257_511_512_513": ([255, 256, 257, 511, 512, 513, 300, 400], 512, 128),
+    # the forward's row-paired q2 (256-row tiles): odd counts, one- and
+    # three-row experts and empty experts between them shift every later
+    # expert's paired rows
+    "paired_odd_and_empty": ([255, 0, 1, 257, 0, 129, 3, 511], 512, 128),
 }
 
 
