@@ -42,7 +42,9 @@ typedef enum {
     MEGAMOE_EINVAL = 1,        /* bad pointer, bad dims, misaligned tensor   */
     MEGAMOE_EUNSUPPORTED = 2,  /* dims outside the supported limits          */
     MEGAMOE_EWORKSPACE = 3,    /* workspace smaller than required            */
-    MEGAMOE_EHIP = 4           /* a HIP runtime call or launch failed        */
+    MEGAMOE_EHIP = 4,          /* a HIP runtime call or launch failed        */
+    MEGAMOE_EDEVICE = 5        /* megamoe_last_error: the device dropped routes
+                                  (expert id outside [0, E))                */
 } megamoe_status;
 
 /* M tokens, hidden size K, E local experts, top_k routes per token, and the
@@ -52,14 +54,19 @@ typedef struct {
     int32_t M, K, E, top_k, I;
 } megamoe_dims;
 
-/* Human-readable text of a status code (static storage). */
+/* Human-readable text of a status code (static storage).  Library plumbing:
+ * the page defines the stages, not an API. */
 const char *megamoe_strerror(int status);
 
 /* Validates dims against the shape limits.  Returns MEGAMOE_OK or an error. */
 int megamoe_check_dims(const megamoe_dims *d);
 
-/* Bytes of workspace megamoe_forward needs (intermediates + error word).
- * megamoe_permute needs only megamoe_permute_workspace_bytes. */
+/* Bytes of workspace megamoe_forward needs: the intermediates the page's
+ * stage overview passes from stage to stage (the FrontReorder metadata and
+ * per-token scales of section 1, GMM1's fp16 output of section 3, SwiGLU's
+ * int8 rows and scales of section 4, GMM2's output of section 5) plus the
+ * device error word.  megamoe_permute needs only
+ * megamoe_permute_workspace_bytes (error word, sort scratch). */
 int megamoe_workspace_bytes(const megamoe_dims *d, size_t *bytes);
 int megamoe_permute_workspace_bytes(const megamoe_dims *d, size_t *bytes);
 
@@ -202,7 +209,12 @@ int megamoe_unpermute(const megamoe_dims *d, const uint16_t *gmm2_out, const flo
 int megamoe_set_overlap(int mode);
 
 /* Synchronises `stream` and reads the number of routes dropped by the last
- * megamoe_permute / megamoe_forward that used this workspace. */
+ * megamoe_permute / megamoe_forward that used this workspace: routes whose
+ * expert id lies outside [0, E).  FrontReorder (section 1) sorts them past
+ * every expert's rows with expanded_row_idx = -1, and the combine of
+ * section 7 skips them, as the page's unpermute combines only valid expanded
+ * rows.  Returns MEGAMOE_OK when none was dropped, MEGAMOE_EDEVICE (with the
+ * count written) when some were, MEGAMOE_EINVAL or MEGAMOE_EHIP otherwise. */
 int megamoe_last_error(const void *workspace, void *stream, int32_t *bad_route_count);
 
 #ifdef __cplusplus

@@ -209,6 +209,7 @@ const char *megamoe_strerror(int status) {
         case MEGAMOE_EUNSUPPORTED: return "dims outside the supported limits";
         case MEGAMOE_EWORKSPACE: return "workspace too small";
         case MEGAMOE_EHIP: return "HIP runtime or launch failure";
+        case MEGAMOE_EDEVICE: return "routes with an expert id outside [0, E) were dropped";
         default: return "unknown status";
     }
 }
@@ -426,7 +427,7 @@ int megamoe_last_error(const void *ws, void *stream, int32_t *bad_route_count) {
         return MEGAMOE_EHIP;
     if (hipStreamSynchronize(s) != hipSuccess) return MEGAMOE_EHIP;
     *bad_route_count = v;
-    return MEGAMOE_OK;
+    return v ? MEGAMOE_EDEVICE : MEGAMOE_OK;
 }
 
 }  // extern "C"

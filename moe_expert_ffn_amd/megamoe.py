@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmegamoe.so")
 
 MEGAMOE_OK = 0
+MEGAMOE_EDEVICE = 5  # megamoe_last_error: routes were dropped
 
 
 class MegaMoEError(RuntimeError):
@@ -229,9 +230,12 @@ def megamoe_unpermute(d, gmm2_out, pts2, expanded_row_idx, probs, out, stream=No
 
 
 def megamoe_last_error(workspace, stream=None) -> int:
+    """The number of routes the last permute / forward on this workspace
+    dropped (the library returns MEGAMOE_EDEVICE when it is not zero)."""
     v = ctypes.c_int32(0)
-    _check("megamoe_last_error", load().megamoe_last_error(_ptr(workspace), _stream(stream),
-                                                           ctypes.byref(v)))
+    rc = load().megamoe_last_error(_ptr(workspace), _stream(stream), ctypes.byref(v))
+    if rc != MEGAMOE_EDEVICE:
+        _check("megamoe_last_error", rc)
     return v.value
 
 

@@ -93,6 +93,7 @@ def test_set_overlap_modes():
 def test_strerror():
     assert MM.strerror(0) == "ok"
     assert "workspace" in MM.strerror(3)
+    assert "dropped" in MM.strerror(MM.MEGAMOE_EDEVICE)
 
 
 # Every device-pointer argument of the compute entry points, by position after

@@ -18,6 +18,7 @@ chain on sampled tokens the oracle evaluates one at a time.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 
 import numpy as np
@@ -346,6 +347,18 @@ def test_dropped_routes_error_word():
     dev2 = H.to_dev(inp2)
     out, dropped = H.run_forward(w, dev2, w1p, w2p)
     assert dropped == 0
+    # the C status: MEGAMOE_EDEVICE with the count when routes were dropped
+    d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
+    ws = torch.empty(MM.megamoe_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda")
+    lib = MM.load()
+    for ids, want_rc, want_n in ((dev["expert_idx"], MM.MEGAMOE_EDEVICE, 3),
+                                 (dev2["expert_idx"], MM.MEGAMOE_OK, 0)):
+        MM.megamoe_forward(d, dev["x"], ids, dev["probs"], w1p, dev["scale1"], w2p,
+                           dev["scale2"], out, ws)
+        n = ctypes.c_int32(-1)
+        rc = lib.megamoe_last_error(ctypes.c_void_p(ws.data_ptr()), None, ctypes.byref(n))
+        assert (rc, n.value) == (want_rc, want_n)
 
 
 def _random_cases(n: int = 32, seed: int = 2024):
