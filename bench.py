@@ -20,8 +20,9 @@ forward rather than during it.)  The same K forwards enqueued back to back witho
 flush are reported beside it.  The per-stage durations (and the roofline of
 the dominant kernel) come from a second timed loop of K flushed steps that
 calls the stage entry points megamoe_forward is made of
-(megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
-megamoe_gmm2, megamoe_unpermute) -- the same kernels, in the same order --
+(megamoe_permute_tokens_paired, megamoe_gmm1_gather,
+megamoe_swiglu_quant_paired, megamoe_gmm2_paired, megamoe_unpermute) -- the
+same kernels, in the same order, with the same row-paired q2 --
 with HIP events recorded on the launch stream between the stages.  The
 forward captured into a HIP graph and replayed is timed as well, and so are
 flushed forwards with SwiGLU inside GMM1's last round (megamoe_set_overlap),
@@ -434,7 +435,8 @@ def main():
     cnt = torch.empty(w.E, dtype=torch.int32, **f)
     cum = torch.empty(w.E, dtype=torch.int32, **f)
     gmC = torch.empty((R, w.N1), dtype=torch.float16, **f)
-    q2 = torch.empty((R, w.I), dtype=torch.int8, **f)
+    prow = torch.empty(R, dtype=torch.int32, **f)
+    q2p = torch.empty(MM.megamoe_paired_q2_bytes(d), dtype=torch.int8, **f)
     pts2 = torch.empty(R, dtype=torch.float32, **f)
     g2 = torch.empty((R, w.K), dtype=torch.float16, **f)
     out = torch.empty((w.M, w.K), dtype=torch.bfloat16, **f)
@@ -445,17 +447,17 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        MM.megamoe_permute_tokens(d, dev["x"], dev["expert_idx"], qx, pts1, eri, srt, cnt, cum,
-                                  pws)
+        MM.megamoe_permute_tokens_paired(d, dev["x"], dev["expert_idx"], qx, pts1, eri, srt,
+                                         cnt, cum, prow, pws)
         if ev is not None:
             ev[1].record(stream)
         MM.megamoe_gmm1_gather(d, qx, srt, cum, w1p, dev["scale1"], gmC)
         if ev is not None:
             ev[2].record(stream)
-        MM.megamoe_swiglu_quant(d, gmC, pts1, cum, q2, pts2)
+        MM.megamoe_swiglu_quant_paired(d, gmC, pts1, cum, prow, q2p, pts2)
         if ev is not None:
             ev[3].record(stream)
-        MM.megamoe_gmm2(d, q2, cum, w2p, dev["scale2"], g2)
+        MM.megamoe_gmm2_paired(d, q2p, cum, w2p, dev["scale2"], g2)
         if ev is not None:
             ev[4].record(stream)
         MM.megamoe_unpermute(d, g2, pts2, eri, dev["probs"], out)

@@ -92,11 +92,12 @@ int megamoe_prepack_w2(const megamoe_dims *d, const int8_t *w2, int8_t *w2p, voi
  *   out        bf16  [M, K]
  *   workspace  >= megamoe_workspace_bytes(); the caller may not touch it while
  *              the forward runs.  Intermediates live there.
- * It runs megamoe_permute_tokens, megamoe_gmm1_gather, megamoe_swiglu_quant,
- * megamoe_gmm2 and megamoe_unpermute in order on the workspace (SwiGLU can
- * start inside GMM1's last round, see megamoe_set_overlap); the result equals, bit
- * for bit, that of the page's five stages (megamoe_permute and megamoe_gmm1
- * in place of the first two). */
+ * It runs megamoe_permute_tokens_paired, megamoe_gmm1_gather,
+ * megamoe_swiglu_quant_paired, megamoe_gmm2_paired and megamoe_unpermute in
+ * order on the workspace (SwiGLU can start inside GMM1's last round, see
+ * megamoe_set_overlap); the result equals, bit for bit, that of the page's
+ * five stages (megamoe_permute, megamoe_gmm1, megamoe_swiglu_quant,
+ * megamoe_gmm2, megamoe_unpermute). */
 int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
                     const float *probs, const int8_t *w1p, const float *scale1,
                     const int8_t *w2p, const float *scale2, uint16_t *out,
@@ -166,6 +167,34 @@ int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert
 int megamoe_gmm1_gather(const megamoe_dims *d, const int8_t *qx, const int32_t *sorted_route,
                         const int32_t *expert_cumsum, const int8_t *w1p, const float *scale1,
                         uint16_t *gmC, int32_t *acc_dbg, void *stream);
+
+/* The forward's SwiGLU -> GMM2 hand-off, as stage entry points (for timing
+ * the forward stage by stage and for tests): q2 in a row-paired layout.
+ * Each expert's rows are padded to an even count, and padded rows 2m and
+ * 2m + 1 share every 128-byte line: row r's 64-byte K slice s sits at byte
+ * ((prow[r] >> 1) * (I / 64) + s) * 128 + (prow[r] & 1) * 64 of q2p, where
+ * prow[r] = r + the number of experts before r's expert with an odd row
+ * count.  GMM2's A copies then read whole lines instead of half lines
+ * (section 5's GMM2 reads the same values; only where they lie differs).
+ *   megamoe_paired_q2_bytes: size of q2p.
+ *   megamoe_permute_tokens_paired: megamoe_permute_tokens, plus prow int32 [R]
+ *     (valid rows only).
+ *   megamoe_swiglu_quant_paired: megamoe_swiglu_quant writing q2p.
+ *   megamoe_gmm2_paired: megamoe_gmm2 reading q2p; results equal those of
+ *     megamoe_gmm2 on the row-major q2 bit for bit. */
+int megamoe_paired_q2_bytes(const megamoe_dims *d, size_t *bytes);
+int megamoe_permute_tokens_paired(const megamoe_dims *d, const uint16_t *x,
+                                  const int32_t *expert_idx, int8_t *qx, float *pts1,
+                                  int32_t *expanded_row_idx, int32_t *sorted_route,
+                                  int32_t *tokens_per_expert, int32_t *expert_cumsum,
+                                  int32_t *prow, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+int megamoe_swiglu_quant_paired(const megamoe_dims *d, const uint16_t *gmC, const float *pts1,
+                                const int32_t *expert_cumsum, const int32_t *prow, int8_t *q2p,
+                                float *pts2, void *stream);
+int megamoe_gmm2_paired(const megamoe_dims *d, const int8_t *q2p, const int32_t *expert_cumsum,
+                        const int8_t *w2p, const float *scale2, uint16_t *gmm2_out,
+                        int32_t *acc_dbg, void *stream);
 
 /* Stage 4 SwiGLU, section 4: per valid row,
  *   c = fp32(gmC) * pts1;  y = silu(c[0:I]) * c[I:2I];  pts2 = max|y| / 127;

@@ -84,6 +84,12 @@ size_t permute_ws_bytes(const megamoe_dims &d) {
            align_up((size_t)d.M * 4);
 }
 
+// bytes of q2 in the row-paired layout: each expert's rows padded to an even
+// count, at most R + E rows
+size_t paired_q2_bytes(const megamoe_dims &d) {
+    return ((size_t)d.M * d.top_k + d.E + 1) * d.I;
+}
+
 Layout forward_layout(const megamoe_dims &d) {
     const size_t R = (size_t)d.M * d.top_k;
     Layout L;
@@ -105,7 +111,7 @@ Layout forward_layout(const megamoe_dims &d) {
     L.gmC = o;    o = align_big(o + R * 2 * d.I * 2);
     // q2, row-paired when GMM2 uses the 256-row tiles: each expert's rows are
     // padded to an even count, at most R + E rows
-    L.q2 = o;     o = align_big(o + (R + d.E + 1) * d.I);
+    L.q2 = o;     o = align_big(o + paired_q2_bytes(d));
     L.g2 = o;     o += align_up(R * d.K * 2);
     L.total = o;
     return L;
@@ -183,20 +189,22 @@ constexpr int kTailSpin = 8192;
 int permute_entry(const megamoe_dims *d, const uint16_t *x, const int32_t *expert_idx,
                   int8_t *gmA, float *pts1, int32_t *eri, int32_t *sorted_route,
                   int32_t *tokens_per_expert, int32_t *expert_cumsum, void *ws, size_t ws_bytes,
-                  bool token_major, void *stream) {
+                  bool token_major, void *stream, int32_t *prow = nullptr) {
     MEGAMOE_TRY(megamoe_check_dims(d));
     const void *ptrs[] = {x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
                           expert_cumsum, ws};
     for (const void *p : ptrs)
         if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (prow && !aligned16(prow)) return MEGAMOE_EINVAL;
     if (ws_bytes < permute_ws_bytes(*d)) return MEGAMOE_EWORKSPACE;
     char *w = (char *)ws;
     const size_t bcnt = align_up(kErrBytes);
     const size_t tsc = bcnt + align_up(route_sort_workspace_bytes(d->M * d->top_k, d->E));
     return run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted_route, tokens_per_expert,
                        expert_cumsum, (int32_t *)w, (int32_t *)(w + bcnt), token_major,
-                       (hipStream_t)stream, (float *)(w + tsc));
+                       (hipStream_t)stream, (float *)(w + tsc), nullptr, nullptr, prow);
 }
+
 
 }  // namespace
 
@@ -341,6 +349,46 @@ int megamoe_gmm2(const megamoe_dims *d, const int8_t *q2, const int32_t *expert_
                    (hipStream_t)stream);
 }
 
+int megamoe_paired_q2_bytes(const megamoe_dims *d, size_t *bytes) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    if (!bytes) return MEGAMOE_EINVAL;
+    *bytes = paired_q2_bytes(*d);
+    return MEGAMOE_OK;
+}
+
+int megamoe_permute_tokens_paired(const megamoe_dims *d, const uint16_t *x,
+                                  const int32_t *expert_idx, int8_t *qx, float *pts1,
+                                  int32_t *eri, int32_t *sorted_route, int32_t *tokens_per_expert,
+                                  int32_t *expert_cumsum, int32_t *prow, void *ws,
+                                  size_t ws_bytes, void *stream) {
+    if (!prow) return MEGAMOE_EINVAL;
+    return permute_entry(d, x, expert_idx, qx, pts1, eri, sorted_route, tokens_per_expert,
+                         expert_cumsum, ws, ws_bytes, true, stream, prow);
+}
+
+int megamoe_swiglu_quant_paired(const megamoe_dims *d, const uint16_t *gmC, const float *pts1,
+                                const int32_t *expert_cumsum, const int32_t *prow, int8_t *q2p,
+                                float *pts2, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {gmC, pts1, expert_cumsum, prow, q2p, pts2};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    return hip_status(launch_swiglu_quant(gmC, pts1, expert_cumsum, d->M * d->top_k, d->E, d->I,
+                                          q2p, pts2, (hipStream_t)stream, nullptr, prow));
+}
+
+int megamoe_gmm2_paired(const megamoe_dims *d, const int8_t *q2p, const int32_t *expert_cumsum,
+                        const int8_t *w2p, const float *scale2, uint16_t *gmm2_out,
+                        int32_t *acc_dbg, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {q2p, expert_cumsum, w2p, scale2, gmm2_out};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (acc_dbg && !aligned16(acc_dbg)) return MEGAMOE_EINVAL;
+    return run_gmm(*d, q2p, expert_cumsum, w2p, scale2, gmm2_out, acc_dbg, d->K, d->I,
+                   (hipStream_t)stream, nullptr, nullptr, true);
+}
+
 int megamoe_unpermute(const megamoe_dims *d, const uint16_t *gmm2_out, const float *pts2,
                       const int32_t *eri, const float *probs, uint16_t *out, void *stream) {
     MEGAMOE_TRY(megamoe_check_dims(d));
@@ -381,11 +429,10 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     const int R = d->M * d->top_k;
     const int overlap = g_overlap.load(std::memory_order_relaxed);
     const bool tail = overlap != 0 && gmm_tail_ok(R, d->E, d->I);
-    // GMM2 with the 256-row tiles reads q2 in the row-paired layout: the
-    // 64-byte K slices of two rows share each 128-byte line, so its A copies
-    // read whole lines (the sort writes each row's paired place to prow)
-    const bool pair = gmm_pick_variant(R, d->E) != 0;
-    int32_t *prow = pair ? (int32_t *)(base + L.prow) : nullptr;
+    // GMM2 reads q2 in the row-paired layout: the 64-byte K slices of two
+    // rows share each 128-byte line, so its A copies read whole lines (the
+    // sort writes each row's paired place to prow)
+    int32_t *prow = (int32_t *)(base + L.prow);
     // the quantised tokens are written once, token-major; GMM1 gathers its
     // expert-sorted rows from them through the route list, so the top_k
     // copies of each token are never written to or re-read from HBM
@@ -409,7 +456,7 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     MEGAMOE_TRY(hip_status(launch_swiglu_quant(gmC, pts1, cumsum, R, d->E, d->I, q2, pts2, s,
                                                tail ? tdone : nullptr, prow)));
     MEGAMOE_TRY(run_gmm(*d, q2, cumsum, w2p, scale2, g2, nullptr, d->K, d->I, s, nullptr, nullptr,
-                        pair));
+                        true));
     return hip_status(launch_unpermute(g2, pts2, eri, probs, d->M, d->K, d->top_k, out, s));
 }
 

@@ -39,8 +39,10 @@ EXPORTED = [
     "megamoe_permute_workspace_bytes", "megamoe_packed_weight_bytes", "megamoe_prepack_w1",
     "megamoe_prepack_w2", "megamoe_forward", "megamoe_permute", "megamoe_permute_tokens",
     "megamoe_permute_noalloc",
-    "megamoe_gmm1", "megamoe_gmm1_gather", "megamoe_swiglu_quant", "megamoe_gmm2", "megamoe_unpermute", "megamoe_last_error",
-    "megamoe_set_overlap",
+    "megamoe_gmm1", "megamoe_gmm1_gather", "megamoe_swiglu_quant", "megamoe_gmm2",
+    "megamoe_unpermute", "megamoe_last_error", "megamoe_set_overlap",
+    "megamoe_paired_q2_bytes", "megamoe_permute_tokens_paired", "megamoe_swiglu_quant_paired",
+    "megamoe_gmm2_paired",
 ]
 
 _lib = None
@@ -84,6 +86,13 @@ def load() -> ctypes.CDLL:
     L.megamoe_last_error.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
     L.megamoe_last_error.restype = i32
     L.megamoe_set_overlap.argtypes, L.megamoe_set_overlap.restype = [i32], i32
+    L.megamoe_paired_q2_bytes.argtypes, L.megamoe_paired_q2_bytes.restype = [D, psz], i32
+    L.megamoe_permute_tokens_paired.argtypes = [D, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.megamoe_permute_tokens_paired.restype = i32
+    L.megamoe_swiglu_quant_paired.argtypes = [D, P, P, P, P, P, P, P]
+    L.megamoe_swiglu_quant_paired.restype = i32
+    L.megamoe_gmm2_paired.argtypes = [D, P, P, P, P, P, P, P]
+    L.megamoe_gmm2_paired.restype = i32
     _lib = L
     return L
 
@@ -218,6 +227,39 @@ def megamoe_swiglu_quant(d, gmC, pts1, expert_cumsum, q2, pts2, stream=None):
 def megamoe_gmm2(d, q2, expert_cumsum, w2p, scale2, gmm2_out, acc_dbg=None, stream=None):
     _check("megamoe_gmm2", load().megamoe_gmm2(
         ctypes.byref(d), _ptr(q2, torch.int8), _ptr(expert_cumsum, torch.int32),
+        _ptr(w2p, torch.int8), _ptr(scale2, torch.float32), _ptr(gmm2_out, torch.float16),
+        _ptr(acc_dbg, torch.int32), _stream(stream)))
+
+
+def megamoe_paired_q2_bytes(d: megamoe_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("megamoe_paired_q2_bytes", load().megamoe_paired_q2_bytes(ctypes.byref(d),
+                                                                     ctypes.byref(n)))
+    return n.value
+
+
+def megamoe_permute_tokens_paired(d, x, expert_idx, qx, pts1, expanded_row_idx, sorted_route,
+                                  tokens_per_expert, expert_cumsum, prow, workspace,
+                                  stream=None):
+    _check("megamoe_permute_tokens_paired", load().megamoe_permute_tokens_paired(
+        ctypes.byref(d), _ptr(x, torch.float16), _ptr(expert_idx, torch.int32),
+        _ptr(qx, torch.int8), _ptr(pts1, torch.float32), _ptr(expanded_row_idx, torch.int32),
+        _ptr(sorted_route, torch.int32), _ptr(tokens_per_expert, torch.int32),
+        _ptr(expert_cumsum, torch.int32), _ptr(prow, torch.int32), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def megamoe_swiglu_quant_paired(d, gmC, pts1, expert_cumsum, prow, q2p, pts2, stream=None):
+    _check("megamoe_swiglu_quant_paired", load().megamoe_swiglu_quant_paired(
+        ctypes.byref(d), _ptr(gmC, torch.float16), _ptr(pts1, torch.float32),
+        _ptr(expert_cumsum, torch.int32), _ptr(prow, torch.int32), _ptr(q2p, torch.int8),
+        _ptr(pts2, torch.float32), _stream(stream)))
+
+
+def megamoe_gmm2_paired(d, q2p, expert_cumsum, w2p, scale2, gmm2_out, acc_dbg=None,
+                        stream=None):
+    _check("megamoe_gmm2_paired", load().megamoe_gmm2_paired(
+        ctypes.byref(d), _ptr(q2p, torch.int8), _ptr(expert_cumsum, torch.int32),
         _ptr(w2p, torch.int8), _ptr(scale2, torch.float32), _ptr(gmm2_out, torch.float16),
         _ptr(acc_dbg, torch.int32), _stream(stream)))
 

@@ -28,12 +28,17 @@ def prepack(d, dev: dict):
     return w1p, w2p
 
 
-def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True, gather: bool = False) -> dict:
+def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True, gather: bool = False,
+               paired: bool = False) -> dict:
     """Each stage through its own entry point; every intermediate returned (device).
 
     gather: the first two stages as the forward runs them
     (megamoe_permute_tokens + megamoe_gmm1_gather); o["qx"] then holds the
-    token-major quantised x and o["gmA"] stays zero."""
+    token-major quantised x and o["gmA"] stays zero.
+    paired (with gather): all stages as the forward runs them, SwiGLU and GMM2
+    passing q2 in the row-paired layout (o["q2p"], o["prow"]; o["q2"] stays
+    zero)."""
+    assert gather or not paired
     d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
     R = w.R
     cu = dict(device="cuda")
@@ -54,6 +59,24 @@ def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True, gather: bool = Fa
         o["acc1"] = torch.zeros((R, w.N1), dtype=torch.int32, **cu)
         o["acc2"] = torch.zeros((R, w.K), dtype=torch.int32, **cu)
     ws = torch.empty(MM.megamoe_permute_workspace_bytes(d), dtype=torch.uint8, **cu)
+    if paired:
+        o["qx"] = torch.zeros((w.M, w.K), dtype=torch.int8, **cu)
+        o["prow"] = torch.full((R,), -1, dtype=torch.int32, **cu)
+        o["q2p"] = torch.zeros(MM.megamoe_paired_q2_bytes(d), dtype=torch.int8, **cu)
+        MM.megamoe_permute_tokens_paired(d, dev["x"], dev["expert_idx"], o["qx"], o["pts1"],
+                                         o["expanded_row_idx"], o["sorted_route"],
+                                         o["tokens_per_expert"], o["expert_cumsum"], o["prow"],
+                                         ws)
+        MM.megamoe_gmm1_gather(d, o["qx"], o["sorted_route"], o["expert_cumsum"], w1p,
+                               dev["scale1"], o["gmC"], o.get("acc1"))
+        MM.megamoe_swiglu_quant_paired(d, o["gmC"], o["pts1"], o["expert_cumsum"], o["prow"],
+                                       o["q2p"], o["pts2"])
+        MM.megamoe_gmm2_paired(d, o["q2p"], o["expert_cumsum"], w2p, dev["scale2"],
+                               o["gmm2_out"], o.get("acc2"))
+        MM.megamoe_unpermute(d, o["gmm2_out"], o["pts2"], o["expanded_row_idx"], dev["probs"],
+                             o["out"])
+        o["dropped"] = MM.megamoe_last_error(ws)
+        return o
     if gather:
         o["qx"] = torch.zeros((w.M, w.K), dtype=torch.int8, **cu)
         MM.megamoe_permute_tokens(d, dev["x"], dev["expert_idx"], o["qx"], o["pts1"],

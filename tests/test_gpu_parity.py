@@ -111,6 +111,7 @@ def test_stages_and_forward_small(w):
     for k in ("gmC", "gmm2_out"):
         assert torch.equal(g_fast[k].view(torch.int16), g[k].view(torch.int16)), k
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    _compare_paired(w, g, H.run_stages(w, dev, w1p, w2p, gather=True, paired=True))
 
 
 def _compare_isolated(w, o_ref, dev, w1p, w2p):
@@ -134,6 +135,34 @@ def _compare_gather(w, g, gg):
     for k in ("gmC", "q2", "gmm2_out"):
         assert torch.equal(gg[k][:Rv].view(torch.int8), g[k][:Rv].view(torch.int8)), k
     assert torch.equal(gg["out"].view(torch.int16), g["out"].view(torch.int16)), "out"
+
+
+def _compare_paired(w, g, gp):
+    """The forward's hand-off from SwiGLU to GMM2 (q2 in the row-paired layout,
+    megamoe_*_paired) against the page's row-major q2: prow is each row plus
+    the number of earlier experts with an odd row count, q2p holds every
+    row's codes where prow puts them, and GMM2 and the combine give the same
+    bits."""
+    for k in ("sorted_route", "expanded_row_idx", "tokens_per_expert", "expert_cumsum"):
+        assert torch.equal(gp[k], g[k]), k
+    Rv = int(g["expert_cumsum"][-1].item()) if w.E else 0
+    counts = g["tokens_per_expert"].cpu().numpy().astype(np.int64)
+    odd_before = np.concatenate([[0], np.cumsum(counts % 2)[:-1]])
+    expert_of_row = np.repeat(np.arange(w.E), counts)
+    want = np.arange(Rv) + odd_before[expert_of_row]
+    prow = gp["prow"][:Rv].cpu().numpy()
+    assert np.array_equal(prow, want), "prow"
+    # row r's 64-byte K slice s at ((prow >> 1) * (I / 64) + s) * 128 + (prow & 1) * 64
+    q2p = gp["q2p"].cpu().numpy()
+    ns = w.I // 64
+    pr = prow.astype(np.int64)
+    base = ((pr >> 1) * ns)[:, None] * 128 + (np.arange(ns) * 128)[None, :] + ((pr & 1) * 64)[:, None]
+    rows = q2p[(base[:, :, None] + np.arange(64)[None, None, :])].reshape(Rv, w.I)
+    assert np.array_equal(rows, g["q2"][:Rv].cpu().numpy()), "q2p rows vs q2"
+    assert torch.equal(gp["pts2"][:Rv], g["pts2"][:Rv]), "pts2"
+    assert torch.equal(gp["acc2"][:Rv], g["acc2"][:Rv]), "acc2"
+    assert torch.equal(gp["gmm2_out"][:Rv].view(torch.int16), g["gmm2_out"][:Rv].view(torch.int16))
+    assert torch.equal(gp["out"].view(torch.int16), g["out"].view(torch.int16)), "out"
 
 
 def test_hot_expert_and_duplicates():
@@ -178,6 +207,7 @@ def test_leftover_tiles_split_by_rows():
     _compare_full(w, inp, o_ref, g)
     _compare_isolated(w, o_ref, dev, w1p, w2p)
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    _compare_paired(w, g, H.run_stages(w, dev, w1p, w2p, gather=True, paired=True))
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == 0
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
@@ -267,6 +297,7 @@ def test_trimmed_grid(shape):
     _compare_full(w, inp, o_ref, g)
     _compare_isolated(w, o_ref, dev, w1p, w2p)
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    _compare_paired(w, g, H.run_stages(w, dev, w1p, w2p, gather=True, paired=True))
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == 0
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
@@ -410,6 +441,7 @@ def test_random_shapes(case):
     assert dropped == o_ref["dropped"]
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    _compare_paired(w, g, H.run_stages(w, dev, w1p, w2p, gather=True, paired=True))
 
 
 def _random_cases_wide(n: int = 60, seed: int = 4242):
@@ -522,6 +554,7 @@ def test_mblock_edges(name):
     _compare_full(w, inp, o_ref, g)
     _compare_isolated(w, o_ref, dev, w1p, w2p)
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    _compare_paired(w, g, H.run_stages(w, dev, w1p, w2p, gather=True, paired=True))
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == 0
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
@@ -581,6 +614,7 @@ def test_full_size_sampled(name):
     del g_fast
     # the forward's gathered GMM1 equals the page's staged GMM1
     _compare_gather(w, g, H.run_stages(w, dev, w1p, w2p, gather=True))
+    _compare_paired(w, g, H.run_stages(w, dev, w1p, w2p, gather=True, paired=True))
 
     # sort metadata: bit-exact everywhere
     srt = O.route_sort(inp["expert_idx"], w.E)
