@@ -20,7 +20,7 @@ forward rather than during it.)  The same K forwards enqueued back to back witho
 flush are reported beside it.  The per-stage durations (and the roofline of
 the dominant kernel) come from a second timed loop of K flushed steps that
 calls the stage entry points megamoe_forward is made of
-(megamoe_permute_tokens_paired, megamoe_gmm1_gather,
+(megamoe_permute_tokens_paired, megamoe_gmm1_gather_split,
 megamoe_swiglu_quant_paired, megamoe_gmm2_paired, megamoe_unpermute) -- the
 same kernels, in the same order, with the same row-paired q2 --
 with HIP events recorded on the launch stream between the stages.  The
@@ -442,6 +442,7 @@ def main():
     out = torch.empty((w.M, w.K), dtype=torch.bfloat16, **f)
     pws = torch.empty(MM.megamoe_permute_workspace_bytes(d), dtype=torch.uint8, **f)
     fws = torch.empty(MM.megamoe_workspace_bytes(d), dtype=torch.uint8, **f)
+    sws = torch.zeros(MM.megamoe_gmm1_split_workspace_bytes(d), dtype=torch.uint8, **f)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -451,7 +452,7 @@ def main():
                                          cnt, cum, prow, pws)
         if ev is not None:
             ev[1].record(stream)
-        MM.megamoe_gmm1_gather(d, qx, srt, cum, w1p, dev["scale1"], gmC)
+        MM.megamoe_gmm1_gather_split(d, qx, srt, cum, w1p, dev["scale1"], gmC, sws)
         if ev is not None:
             ev[2].record(stream)
         MM.megamoe_swiglu_quant_paired(d, gmC, pts1, cum, prow, q2p, pts2)

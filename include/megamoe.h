@@ -92,7 +92,7 @@ int megamoe_prepack_w2(const megamoe_dims *d, const int8_t *w2, int8_t *w2p, voi
  *   out        bf16  [M, K]
  *   workspace  >= megamoe_workspace_bytes(); the caller may not touch it while
  *              the forward runs.  Intermediates live there.
- * It runs megamoe_permute_tokens_paired, megamoe_gmm1_gather,
+ * It runs megamoe_permute_tokens_paired, megamoe_gmm1_gather_split,
  * megamoe_swiglu_quant_paired, megamoe_gmm2_paired and megamoe_unpermute in
  * order on the workspace (SwiGLU can start inside GMM1's last round, see
  * megamoe_set_overlap); the result equals, bit for bit, that of the page's
@@ -167,6 +167,24 @@ int megamoe_gmm1(const megamoe_dims *d, const int8_t *gmA, const int32_t *expert
 int megamoe_gmm1_gather(const megamoe_dims *d, const int8_t *qx, const int32_t *sorted_route,
                         const int32_t *expert_cumsum, const int8_t *w1p, const float *scale1,
                         uint16_t *gmC, int32_t *acc_dbg, void *stream);
+
+/* megamoe_gmm1_gather as megamoe_forward runs it, with a buffer for the
+ * GEMM's sparse last round: when fewer tiles are left for the last round
+ * than groups of four workgroups are idle, each leftover tile is multiplied
+ * by four workgroups over a quarter of K each, and the last of them adds the
+ * four int32 partial tiles (an exact integer sum, section 3's acc) and stores
+ * the tile.  Results equal megamoe_gmm1_gather's bit for bit.
+ *   megamoe_gmm1_split_workspace_bytes: size of split_ws (about 64 MB).
+ *   split_ws  device, zero-filled before its first use; each call leaves it
+ *             ready for the next (its counters back at zero).  Calls that
+ *             overlap in time on one split_ws race; give concurrent streams
+ *             a buffer each.
+ * The other arguments are those of megamoe_gmm1_gather (no acc_dbg). */
+int megamoe_gmm1_split_workspace_bytes(const megamoe_dims *d, size_t *bytes);
+int megamoe_gmm1_gather_split(const megamoe_dims *d, const int8_t *qx,
+                              const int32_t *sorted_route, const int32_t *expert_cumsum,
+                              const int8_t *w1p, const float *scale1, uint16_t *gmC,
+                              void *split_ws, size_t split_ws_bytes, void *stream);
 
 /* The forward's SwiGLU -> GMM2 hand-off, as stage entry points (for timing
  * the forward stage by stage and for tests): q2 in a row-paired layout.

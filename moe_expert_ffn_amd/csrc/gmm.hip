@@ -443,6 +443,54 @@ __device__ __forceinline__ int fresh_lane_id() {
 // Since the ring is not used, the next tile's first copies can be in flight
 // while these stores go out.  Returns the number of store instructions
 // issued (wave-uniform).
+// rows 16 i .. 16 i + 15 of a wave's sub-tile from the lane's accumulators
+// a[TN] of them (MFMA layout); returns the store instructions issued
+template <int TN>
+__device__ __forceinline__ int store_group(const GmmParams &p, const v4i (&a)[TN], int i,
+                                           const float *s_sc, int row0, int n0, int wm0, int wn0,
+                                           int8_t *wbuf, int r_lo, int r_hi, int lane) {
+    const int rb0 = wm0 + 16 * i;  // tile row of the first row
+    uint2 h[TN];  // fp16 of the lane's values of row 16 i + (lane & 15), two per word
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const float4 s4 = *reinterpret_cast<const float4 *>(s_sc + wn0 + 16 * j + 4 * (lane >> 4));
+        const uint32_t h0 = f2h(keep_f32((float)a[j][0] * s4.x));
+        const uint32_t h1 = f2h(keep_f32((float)a[j][1] * s4.y));
+        const uint32_t h2 = f2h(keep_f32((float)a[j][2] * s4.z));
+        const uint32_t h3 = f2h(keep_f32((float)a[j][3] * s4.w));
+        h[j] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+    }
+    int nstores = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int rb = rb0 + 8 * half;  // tile row of the chunk's first row
+        if (rb + 8 <= r_lo || rb >= r_hi) continue;
+        // lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3
+        if (((lane >> 3) & 1) == half) {
+            const int rr = lane & 7;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int c = 2 * j + (lane >> 5);  // 16-byte piece of the row
+                *reinterpret_cast<uint2 *>(wbuf + rr * 128 + ((c ^ rr) << 4) +
+                                           (((lane >> 4) & 1) << 3)) = h[j];
+            }
+        }
+        const int rr = lane >> 3, c = lane & 7;
+        const uint4 v = *reinterpret_cast<const uint4 *>(wbuf + rr * 128 + ((c ^ rr) << 4));
+        const int r = rb + rr;
+        // at least one row of the chunk is stored, so the instruction issues
+        if (r >= r_lo && r < r_hi) store_nt16(p.C + (size_t)(row0 + r) * p.N + n0 + wn0 + 8 * c, v);
+        ++nstores;
+    }
+    return nstores;
+}
+
+// whether rows 16 i .. 16 i + 15 of a wave's sub-tile hold an output row
+__device__ __forceinline__ bool group_live(int i, int wm0, int r_lo, int r_hi) {
+    const int rb0 = wm0 + 16 * i;
+    return rb0 + 16 > r_lo && rb0 < r_hi;
+}
+
 template <int TM, int TN>
 __device__ __forceinline__ int store_tile_private(const GmmParams &p, const v4i (&acc)[TM][TN],
                                                   const float *s_sc, int row0, int n0, int wm0,
@@ -453,44 +501,77 @@ __device__ __forceinline__ int store_tile_private(const GmmParams &p, const v4i 
     if (!live || n0 + wn0 >= p.N) return 0;
     const int lane = fresh_lane_id();
     int nstores = 0;
-    // rows 16 i .. 16 i + 15 of the sub-tile: chunks 2 i and 2 i + 1
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        if (group_live(i, wm0, r_lo, r_hi))
+            nstores += store_group<TN>(p, acc[i], i, s_sc, row0, n0, wm0, wn0, wbuf, r_lo, r_hi,
+                                       lane);
+    return nstores;
+}
+
+// A K piece of a leftover tile (sparse last round, GMM1 of the forward): the
+// tile's NP pieces each multiply a quarter of K and store their int32
+// partial tile to ks_part; the last piece to count itself adds the NP
+// partials (integer sums: exact, in any order) and stores the tile as
+// store_tile_private does.  No piece waits for another.  The protocol is
+// release / acquire at device scope around a system-scope counter: each
+// piece's partial is written back from its XCD's L2 before it counts itself,
+// and the last piece invalidates its caches before it reads the partials.
+// It also puts the counter back to zero, so a buffer zeroed once serves every
+// later launch.  The last piece reads its own partial back too, so that its accumulators
+// are free during the sums (the K loop leaves no register for another copy
+// of them).  Returns the store instructions issued.
+template <int TM, int TN, int NW, int NP>
+__device__ __forceinline__ int ks_store_tile(const GmmParams &p, const v4i (&acc)[TM][TN], int jj,
+                                             int piece, int wave, const float *s_sc, int row0,
+                                             int n0, int wm0, int wn0, int8_t *wbuf, int r_lo,
+                                             int r_hi, bool live, int *s_flag) {
+    constexpr int kPiece = NW * TM * TN * kWave;  // 16-byte units of one partial tile
+    static_assert(kPiece * 16 <= (int)kKsPartBytes, "partial tile size");
+    live = live && n0 + wn0 < p.N;
+    const int lane = fresh_lane_id();
+    // [piece][wave][16x16 block][lane]: each store writes 1 KB
+    const v4i *part = reinterpret_cast<const v4i *>(p.ks_part) + (size_t)jj * NP * kPiece +
+                      (size_t)wave * TM * TN * kWave + lane;
+    // a wave without an output row neither writes nor reads
+    if (live) {
+        v4i *mine = const_cast<v4i *>(part) + (size_t)piece * kPiece;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) mine[(i * TN + j) * kWave] = acc[i][j];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is in L2
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        *s_flag = (int)__hip_atomic_fetch_add(p.ks_count + jj, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM);
+        if (*s_flag == NP - 1) {
+            // every piece has counted: the counter is free for the next launch
+            __hip_atomic_store(p.ks_count + jj, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+    }
+    __syncthreads();
+    if (*s_flag != NP - 1 || !live) return 0;  // another piece of the tile stores it
+    int nstores = 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int rb0 = wm0 + 16 * i;  // tile row of the first row
-        if (rb0 + 16 <= r_lo || rb0 >= r_hi) continue;  // no output row in these chunks
-        uint2 h[TN];  // fp16 of the lane's values of row 16 i + (lane & 15), two per word
+        if (!group_live(i, wm0, r_lo, r_hi)) continue;
+        // one row group's loads at a time: hoisted above the previous group's
+        // stores, they would not fit in the registers
+        asm volatile("" ::: "memory");
+        v4i t[NP][TN];  // the pieces' blocks of row group i, all requested together
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const float4 s4 =
-                *reinterpret_cast<const float4 *>(s_sc + wn0 + 16 * j + 4 * (lane >> 4));
-            const uint32_t h0 = f2h(keep_f32((float)acc[i][j][0] * s4.x));
-            const uint32_t h1 = f2h(keep_f32((float)acc[i][j][1] * s4.y));
-            const uint32_t h2 = f2h(keep_f32((float)acc[i][j][2] * s4.z));
-            const uint32_t h3 = f2h(keep_f32((float)acc[i][j][3] * s4.w));
-            h[j] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        }
+        for (int q = 0; q < NP; ++q)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int rb = rb0 + 8 * half;  // tile row of the chunk's first row
-            if (rb + 8 <= r_lo || rb >= r_hi) continue;
-            // lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3
-            if (((lane >> 3) & 1) == half) {
-                const int rr = lane & 7;
+            for (int j = 0; j < TN; ++j) t[q][j] = part[(size_t)q * kPiece + (i * TN + j) * kWave];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int c = 2 * j + (lane >> 5);  // 16-byte piece of the row
-                    *reinterpret_cast<uint2 *>(wbuf + rr * 128 + ((c ^ rr) << 4) +
-                                               (((lane >> 4) & 1) << 3)) = h[j];
-                }
-            }
-            const int rr = lane >> 3, c = lane & 7;
-            const uint4 v = *reinterpret_cast<const uint4 *>(wbuf + rr * 128 + ((c ^ rr) << 4));
-            const int r = rb + rr;
-            // at least one row of the chunk is stored, so the instruction issues
-            if (r >= r_lo && r < r_hi)
-                store_nt16(p.C + (size_t)(row0 + r) * p.N + n0 + wn0 + 8 * c, v);
-            ++nstores;
-        }
+        for (int q = 1; q < NP; ++q)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) t[0][j] += t[q][j];
+        nstores += store_group<TN>(p, t[0], i, s_sc, row0, n0, wm0, wn0, wbuf, r_lo, r_hi, lane);
     }
     return nstores;
 }
@@ -622,6 +703,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         extra = j < L ? F * G + j : -1;
         piece = slot % WAVES_M;
     }
+    // With a partial-tile buffer (the forward's GMM1), the pieces of a
+    // leftover tile split its K slices instead of its rows: each runs a
+    // quarter of the K chain that bounds a row piece, and the last of them
+    // adds the partial tiles (ks_combine).
+    const bool ksplit = ranked && p.ks_part != nullptr && p.acc_dbg == nullptr &&
+                        nst % (2 * WAVES_M) == 0 && L <= kKsMaxTiles;
 
     // SwiGLU in the last round (GMM1 of the forward; tiles of unequal cost).
     // Kept in LDS and read once per tile: the K loop has no scalar register
@@ -645,9 +732,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     struct TileSetup {
         int valid, e, row0, rows, n0;
         bool piece_tile;
-        const int8_t *btile;
+        int kcnt;             // K slices of this tile (a K piece: a quarter)
+        const int8_t *abase;  // A at the tile's first K slice
+        const int8_t *btile;  // the tile's weights at its first K slice
         uint32_t voff[LPW];
     };
+    // bytes between the A operand's K slices of one row
+    const int a_stage = p.a_pair ? 2 * kBK64 : kBK64;
     // packed weights are K-slice-major: the block of (expert e, n-block
     // nblk) for K slice ks sits at ((ks * E + e) * NB + nblk) blocks
     const size_t bstep = (size_t)p.E * NB * kPackBlock;
@@ -660,18 +751,25 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         ts.row0 = tr.row0;
         ts.rows = tr.rows;
         ts.n0 = tr.nblk * BN;
-        // a row piece of a leftover tile: rows [plo, phi] of the tile
+        // a piece of a leftover tile: rows [plo, phi] of the tile (a row
+        // piece), or every row and a quarter of the K slices (a K piece)
         ts.piece_tile = ranked && kk == F;
-        const int plo = piece * WM, phi = min(plo + WM, tr.rows) - 1;
-        if (ts.piece_tile && plo >= tr.rows) return ts;
+        const bool kpiece = ts.piece_tile && ksplit;
+        const bool rpiece = ts.piece_tile && !ksplit;
+        const int plo = rpiece ? piece * WM : 0;
+        const int phi = rpiece ? min(plo + WM, tr.rows) - 1 : min(tr.rows, BM) - 1;
+        if (rpiece && plo >= tr.rows) return ts;
         ts.valid = 1;
+        const int kbeg = kpiece ? piece * (nst / WAVES_M) : 0;
+        ts.kcnt = kpiece ? nst / WAVES_M : nst;
+        ts.abase = p.A + (size_t)kbeg * a_stage;
         if (threadIdx.x == 0) {
             s_tile[par][0] = tr.row0;
             s_tile[par][1] = tr.rows;
             s_tile[par][2] = ts.n0;
-            s_tile[par][3] = ts.piece_tile ? plo : 0;
-            s_tile[par][4] = ts.piece_tile ? phi + 1 : min(tr.rows, BM);
-            s_tile[par][5] = ts.piece_tile;
+            s_tile[par][3] = plo;
+            s_tile[par][4] = phi + 1;
+            s_tile[par][5] = kpiece ? 2 : (rpiece ? 1 : 0);  // whole, row piece, K piece
         }
 
         // scales of the tile's columns (clamped: columns past N are never stored)
@@ -685,14 +783,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         // results are not stored).
         // per-lane 32-bit source offsets: from p.A for the A rows, from the
         // tile's first weight block for the weights
-        ts.btile = p.B + ((size_t)tr.e * NB + tr.nblk) * kPackBlock;
+        ts.btile = p.B + ((size_t)tr.e * NB + tr.nblk) * kPackBlock + (size_t)kbeg * bstep;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int pch = (wave + j * NW) * 64 + lane;
             if (j < kAJ) {
                 const int r = pch >> 2, kc = (pch & 3) ^ swz64(pch >> 2);
                 const int arow =
-                    tr.row0 + (ts.piece_tile ? min(max(r, plo), phi) : min(r, tr.rows - 1));
+                    tr.row0 + (rpiece ? min(max(r, plo), phi) : min(r, tr.rows - 1));
                 if (p.a_pair) {  // padded row g: 64-byte K slices of rows 2m, 2m + 1 share a line
                     const int g = arow + s_pad[tr.e];
                     ts.voff[j] = (uint32_t)(g >> 1) * (uint32_t)(2 * Kred) + (g & 1) * 64 + kc * 16;
@@ -709,13 +807,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         return ts;
     };
 
-    // bytes between the A operand's K slices of one row
-    const int a_stage = p.a_pair ? 2 * kBK64 : kBK64;
     // the copies of K slice `stage` of tile t into its ring slot
     auto issue = [&](const TileSetup &t, int stage) {
-        if (stage >= nst) return;
+        if (stage >= t.kcnt) return;
         const uint32_t sbase = ring + (uint32_t)((stage % NS) * kStage);
-        const int8_t *abase = p.A + (size_t)stage * a_stage;
+        const int8_t *abase = t.abase + (size_t)stage * a_stage;
         const int8_t *bbase = t.btile + (size_t)stage * bstep;
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
@@ -740,12 +836,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     TileSetup cur = setup(0, 0);
     if (cur.valid) {
         issue_first(cur);
-        if (nst >= NS) wait_vmcnt<(NS - 1) * LPW>();
+        if (cur.kcnt >= NS) wait_vmcnt<(NS - 1) * LPW>();
         else wait_vmcnt<0>();
     }
     for (int k = 0; cur.valid; ++k, parity ^= 1) {
         const int rows = cur.rows;
         const bool piece_tile = cur.piece_tile;
+        const int kcnt = cur.kcnt;
 
         v4i acc[TM][TN];
 #pragma unroll
@@ -780,7 +877,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             // the NS-2 after kt+1 may be in flight (the previous tile's
             // epilogue stores are older than stage 1, so they are done too)
             auto await_next = [&](int kt) {
-                if (kt + NS - 1 < nst) wait_vmcnt<(NS - 2) * LPW>();
+                if (kt + NS - 1 < kcnt) wait_vmcnt<(NS - 2) * LPW>();
                 else wait_vmcnt<0>();
                 __syncthreads();
             };
@@ -788,8 +885,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
             frag(0, fa[0], fb[0]);
 
             // two stages per trip so that the register set of every stage is
-            // known at compile time (set = stage & 1); nst is even
-            for (int kt0 = 0; kt0 < nst; kt0 += 2) {
+            // known at compile time (set = stage & 1); kcnt is even
+            for (int kt0 = 0; kt0 < kcnt; kt0 += 2) {
                 static_for<0, 2>([&](auto uc) {
                     constexpr int rs = decltype(uc)::value, rn = rs ^ 1;  // register sets
                     const int kt = kt0 + rs;
@@ -809,7 +906,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         };
         // a row piece of a leftover tile: only its wave row block multiplies
         // and stores (the other pieces of the tile run on other workgroups)
-        const bool piece_live = !piece_tile || wave / WAVES_N == piece;
+        const bool piece_live = !piece_tile || ksplit || wave / WAVES_N == piece;
         if ((!SKIP || wm0 < rows) && piece_live) kloop(std::true_type{});
         else kloop(std::false_type{});
 
@@ -820,8 +917,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         const int t_n0 = __builtin_amdgcn_readfirstlane(s_tile[parity][2]);
         const int r_lo = __builtin_amdgcn_readfirstlane(s_tile[parity][3]);
         const int r_hi = __builtin_amdgcn_readfirstlane(s_tile[parity][4]);
-        const bool t_piece = __builtin_amdgcn_readfirstlane(s_tile[parity][5]) != 0;
-        const bool live = (!t_piece || wave / WAVES_N == piece) && wm0 < t_rows;
+        const int t_kind = __builtin_amdgcn_readfirstlane(s_tile[parity][5]);
+        const bool live = (t_kind != 1 || wave / WAVES_N == piece) && wm0 < t_rows;
         // the debug int32 accumulators go straight from the registers, before
         // the next tile's copies, so the wait for its first stage covers them
         if (p.acc_dbg && live) store_acc_dbg<TM, TN>(p, acc, t_row0, t_rows, t_n0, wm0, wn0, lane);
@@ -832,13 +929,20 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
         // and only the wait for stage 0 allows for them.
         __syncthreads();  // every wave has read its last fragments: the ring is free
         if (nxt.valid) issue(nxt, 0);
-        const int nstores = store_tile_private<TM, TN>(p, acc, s_scale[parity], t_row0, t_n0, wm0,
-                                                       wn0, s_wbuf[wave], r_lo, r_hi, live);
+        // a K piece (which has no next tile): the last of its tile's pieces stores
+        int nstores;
+        if (TRIM || t_kind != 2)
+            nstores = store_tile_private<TM, TN>(p, acc, s_scale[parity], t_row0, t_n0, wm0, wn0,
+                                                 s_wbuf[wave], r_lo, r_hi, live);
+        else
+            nstores = ks_store_tile<TM, TN, NW, WAVES_M>(
+                p, acc, extra - F * G, piece, wave, s_scale[parity], t_row0, t_n0, wm0, wn0,
+                s_wbuf[wave], r_lo, r_hi, live, &s_go);
         if (nxt.valid) {
 #pragma unroll
             for (int st = 1; st < NS; ++st) issue(nxt, st);
             // stage 0 (and the tile's older scale copy) has landed
-            if (nst >= NS) wait_vmcnt_plus<(NS - 1) * LPW>(nstores);
+            if (nxt.kcnt >= NS) wait_vmcnt_plus<(NS - 1) * LPW>(nstores);
             else wait_vmcnt<0>();
         }
         if constexpr (!TRIM) {

@@ -6,6 +6,14 @@
 
 namespace megamoe {
 
+// K-split last round of the 256-row GEMM: at most this many leftover tiles,
+// each in 4 pieces whose int32 partial tiles are 256 KB
+constexpr int kKsMaxTiles = 64;
+constexpr size_t kKsPartBytes = 256 * 256 * 4;
+// words of the forward's sync array: 3 for SwiGLU in GMM1's last round, then
+// one counter per K-split leftover tile; the permute zeroes them
+constexpr int kSyncWords = 3 + kKsMaxTiles;
+
 struct GmmParams {
     const int8_t *A;          // [rows, Kred] expert-major activations
     const int8_t *B;          // packed weights [E][N][Kred]
@@ -24,11 +32,17 @@ struct GmmParams {
     int8_t *tail_q2 = nullptr;        // [R, tail_I] int8
     float *tail_pts2 = nullptr;       // [R]
     const float *tail_pts1 = nullptr; // [R]
-    uint32_t *tail_sync = nullptr;    // [3] counters of the last-round SwiGLU
+    uint32_t *tail_sync = nullptr;    // [kSyncWords]: 3 counters of the last-round SwiGLU
     uint8_t *tail_done = nullptr;     // [R] set for each row the last round did
     int tail_I = 0;
     int tail_spin = 0;                // poll limit of the wait; < 0: give up at once
     const int32_t *tail_prow = nullptr;  // nullable: q2 row-paired (see a_pair), row r at tail_prow[r]
+    // GMM1 of the forward, nullable: a sparse last round's leftover tiles are
+    // split over K instead of into row pieces (see gmm.hip).  ks_part holds
+    // kKsMaxTiles x 4 int32 partial tiles (kKsPartBytes each); ks_count
+    // kKsMaxTiles counters, zero at launch (the kernel leaves them at zero).
+    int32_t *ks_part = nullptr;
+    uint32_t *ks_count = nullptr;
     // A in the row-paired layout (GEMMs without a_route): every expert's group
     // is padded to an even row count, and padded rows 2m and 2m + 1 share each
     // 128-byte line, [Rp / 2][Kred / 64][2][64] bytes.  A copy instruction of

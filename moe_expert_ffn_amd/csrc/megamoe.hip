@@ -74,7 +74,7 @@ int32_t *scratch_device_ptr() {
 
 struct Layout {
     size_t err, bcnt, tscale, tsync, tdone, eri, sorted, counts, cumsum, pts1, pts2, prow, gmA,
-        gmC, q2, g2, total;
+        gmC, q2, g2, ks, total;
 };
 
 // permute workspace: error word, the sort's per-block expert counts, then the
@@ -83,6 +83,12 @@ size_t permute_ws_bytes(const megamoe_dims &d) {
     return align_up(kErrBytes) + align_up(route_sort_workspace_bytes(d.M * d.top_k, d.E)) +
            align_up((size_t)d.M * 4);
 }
+
+// GMM1's K-split buffer (megamoe_gmm1_gather_split): the tile counters, then
+// the partial tiles
+constexpr size_t kSplitCountBytes = 256;
+static_assert(kKsMaxTiles * 4 <= (int)kSplitCountBytes, "counter block");
+size_t split_ws_bytes() { return kSplitCountBytes + (size_t)kKsMaxTiles * 4 * kKsPartBytes; }
 
 // bytes of q2 in the row-paired layout: each expert's rows padded to an even
 // count, at most R + E rows
@@ -97,7 +103,7 @@ Layout forward_layout(const megamoe_dims &d) {
     L.err = o;    o += align_up(kErrBytes);
     L.bcnt = o;   o += align_up(route_sort_workspace_bytes((int)R, d.E));
     L.tscale = o; o += align_up((size_t)d.M * 4);
-    L.tsync = o;  o += align_up(3 * 4);
+    L.tsync = o;  o += align_up(kSyncWords * 4);
     L.tdone = o;  o += align_up(R);
     L.eri = o;    o += align_up(R * 4);
     L.sorted = o; o += align_up(R * 4);
@@ -112,7 +118,9 @@ Layout forward_layout(const megamoe_dims &d) {
     // q2, row-paired when GMM2 uses the 256-row tiles: each expert's rows are
     // padded to an even count, at most R + E rows
     L.q2 = o;     o = align_big(o + paired_q2_bytes(d));
-    L.g2 = o;     o += align_up(R * d.K * 2);
+    L.g2 = o;     o = align_big(o + R * d.K * 2);
+    // GMM1's partial tiles when its sparse last round splits tiles over K
+    L.ks = o;     o += (size_t)kKsMaxTiles * 4 * kKsPartBytes;
     L.total = o;
     return L;
 }
@@ -153,7 +161,8 @@ int run_permute(const megamoe_dims &d, const uint16_t *x, const int32_t *expert_
 }
 
 // a_route (nullable): A row d is token a_route[d] / top_k of a token-major A.
-// tail (nullable, GMM1 only): SwiGLU in GMM1's last round, see gmm.hip.
+// tail (nullable, GMM1 only): SwiGLU in GMM1's last round (tail_*) or the
+// K-split last round (ks_*), see gmm.hip.
 // a_pair: A is in the row-paired layout (GmmParams::a_pair).
 int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const int8_t *Bp,
             const float *scale, uint16_t *C, int32_t *dbg, int N, int Kred, hipStream_t s,
@@ -171,6 +180,8 @@ int run_gmm(const megamoe_dims &d, const int8_t *A, const int32_t *cumsum, const
         prm.tail_I = tail->tail_I;
         prm.tail_spin = tail->tail_spin;
         prm.tail_prow = tail->tail_prow;
+        prm.ks_part = tail->ks_part;
+        prm.ks_count = tail->ks_count;
     }
     return hip_status(launch_gmm(gmm_pick_variant(R, d.E), prm, R, cu_count_current(), s));
 }
@@ -349,6 +360,29 @@ int megamoe_gmm2(const megamoe_dims *d, const int8_t *q2, const int32_t *expert_
                    (hipStream_t)stream);
 }
 
+int megamoe_gmm1_split_workspace_bytes(const megamoe_dims *d, size_t *bytes) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    if (!bytes) return MEGAMOE_EINVAL;
+    *bytes = split_ws_bytes();
+    return MEGAMOE_OK;
+}
+
+int megamoe_gmm1_gather_split(const megamoe_dims *d, const int8_t *qx,
+                              const int32_t *sorted_route, const int32_t *expert_cumsum,
+                              const int8_t *w1p, const float *scale1, uint16_t *gmC,
+                              void *split_ws, size_t split_ws_bytes_, void *stream) {
+    MEGAMOE_TRY(megamoe_check_dims(d));
+    const void *ptrs[] = {qx, sorted_route, expert_cumsum, w1p, scale1, gmC, split_ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MEGAMOE_EINVAL;
+    if (split_ws_bytes_ < split_ws_bytes()) return MEGAMOE_EWORKSPACE;
+    GmmParams kp{};
+    kp.ks_count = (uint32_t *)split_ws;
+    kp.ks_part = (int32_t *)((char *)split_ws + kSplitCountBytes);
+    return run_gmm(*d, qx, expert_cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K,
+                   (hipStream_t)stream, sorted_route, &kp);
+}
+
 int megamoe_paired_q2_bytes(const megamoe_dims *d, size_t *bytes) {
     MEGAMOE_TRY(megamoe_check_dims(d));
     if (!bytes) return MEGAMOE_EINVAL;
@@ -437,8 +471,8 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     // expert-sorted rows from them through the route list, so the top_k
     // copies of each token are never written to or re-read from HBM
     MEGAMOE_TRY(run_permute(*d, x, expert_idx, gmA, pts1, eri, sorted, counts, cumsum, err, bcnt,
-                            true, s, (float *)(base + L.tscale), tail ? tdone : nullptr,
-                            tail ? tsync : nullptr, prow));
+                            true, s, (float *)(base + L.tscale), tail ? tdone : nullptr, tsync,
+                            prow));
     // SwiGLU: the rows whose GMM1 output is complete before GMM1's last round
     // are done by the workgroups left idle in that round; the SwiGLU kernel
     // does the rest (all rows without the overlap)
@@ -451,8 +485,13 @@ int megamoe_forward(const megamoe_dims *d, const uint16_t *x, const int32_t *exp
     tp.tail_I = d->I;
     tp.tail_spin = overlap == 2 ? -1 : kTailSpin;
     tp.tail_prow = prow;
+    // without the overlap, GMM1's sparse last round splits its tiles over K
+    // (the permute zeroes the counters after the overlap's three words)
+    GmmParams kp{};
+    kp.ks_part = (int32_t *)(base + L.ks);
+    kp.ks_count = tsync + 3;
     MEGAMOE_TRY(run_gmm(*d, gmA, cumsum, w1p, scale1, gmC, nullptr, 2 * d->I, d->K, s, sorted,
-                        tail ? &tp : nullptr));
+                        tail ? &tp : &kp));
     MEGAMOE_TRY(hip_status(launch_swiglu_quant(gmC, pts1, cumsum, R, d->E, d->I, q2, pts2, s,
                                                tail ? tdone : nullptr, prow)));
     MEGAMOE_TRY(run_gmm(*d, q2, cumsum, w2p, scale2, g2, nullptr, d->K, d->I, s, nullptr, nullptr,

@@ -249,10 +249,8 @@ __global__ __launch_bounds__(kSortBlock) void route_scatter_kernel(
     __syncthreads();
     const int valid_rows = s_valid;
     if (b == 0) {
-        if (tid == 0) {
-            err_word[0] = R - valid_rows;
-            if (tail_sync) tail_sync[0] = tail_sync[1] = tail_sync[2] = 0;
-        }
+        if (tid == 0) err_word[0] = R - valid_rows;
+        if (tail_sync && tid < kSyncWords) tail_sync[tid] = 0;
         for (int d = valid_rows + tid; d < R; d += kSortBlock) sorted_route[d] = -1;
     }
 
@@ -432,7 +430,7 @@ __global__ __launch_bounds__(256) void permute_fused_kernel(
     const int r_own = t * top_k;
     // clear the flags of the GMM1 that follows (route r's flag is row r's)
     if (tail_done && tid < top_k) tail_done[r_own + tid] = 0;
-    if (tail_sync && t == 0 && tid < 3) tail_sync[tid] = 0;
+    if (tail_sync && t == 0 && tid < kSyncWords) tail_sync[tid] = 0;
 
     // Every first load is issued up front: the token's row, the first 2048
     // expert ids (all of them up to R = 2048) and the token's own ids.

@@ -42,7 +42,7 @@ EXPORTED = [
     "megamoe_gmm1", "megamoe_gmm1_gather", "megamoe_swiglu_quant", "megamoe_gmm2",
     "megamoe_unpermute", "megamoe_last_error", "megamoe_set_overlap",
     "megamoe_paired_q2_bytes", "megamoe_permute_tokens_paired", "megamoe_swiglu_quant_paired",
-    "megamoe_gmm2_paired",
+    "megamoe_gmm2_paired", "megamoe_gmm1_split_workspace_bytes", "megamoe_gmm1_gather_split",
 ]
 
 _lib = None
@@ -87,6 +87,10 @@ def load() -> ctypes.CDLL:
     L.megamoe_last_error.restype = i32
     L.megamoe_set_overlap.argtypes, L.megamoe_set_overlap.restype = [i32], i32
     L.megamoe_paired_q2_bytes.argtypes, L.megamoe_paired_q2_bytes.restype = [D, psz], i32
+    L.megamoe_gmm1_split_workspace_bytes.argtypes = [D, psz]
+    L.megamoe_gmm1_split_workspace_bytes.restype = i32
+    L.megamoe_gmm1_gather_split.argtypes = [D, P, P, P, P, P, P, P, sz, P]
+    L.megamoe_gmm1_gather_split.restype = i32
     L.megamoe_permute_tokens_paired.argtypes = [D, P, P, P, P, P, P, P, P, P, P, sz, P]
     L.megamoe_permute_tokens_paired.restype = i32
     L.megamoe_swiglu_quant_paired.argtypes = [D, P, P, P, P, P, P, P]
@@ -229,6 +233,22 @@ def megamoe_gmm2(d, q2, expert_cumsum, w2p, scale2, gmm2_out, acc_dbg=None, stre
         ctypes.byref(d), _ptr(q2, torch.int8), _ptr(expert_cumsum, torch.int32),
         _ptr(w2p, torch.int8), _ptr(scale2, torch.float32), _ptr(gmm2_out, torch.float16),
         _ptr(acc_dbg, torch.int32), _stream(stream)))
+
+
+def megamoe_gmm1_split_workspace_bytes(d: megamoe_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("megamoe_gmm1_split_workspace_bytes",
+           load().megamoe_gmm1_split_workspace_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def megamoe_gmm1_gather_split(d, qx, sorted_route, expert_cumsum, w1p, scale1, gmC, split_ws,
+                              stream=None):
+    _check("megamoe_gmm1_gather_split", load().megamoe_gmm1_gather_split(
+        ctypes.byref(d), _ptr(qx, torch.int8), _ptr(sorted_route, torch.int32),
+        _ptr(expert_cumsum, torch.int32), _ptr(w1p, torch.int8), _ptr(scale1, torch.float32),
+        _ptr(gmC, torch.float16), _ptr(split_ws, torch.uint8), split_ws.numel(),
+        _stream(stream)))
 
 
 def megamoe_paired_q2_bytes(d: megamoe_dims) -> int:

@@ -37,7 +37,8 @@ def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True, gather: bool = Fa
     token-major quantised x and o["gmA"] stays zero.
     paired (with gather): all stages as the forward runs them, SwiGLU and GMM2
     passing q2 in the row-paired layout (o["q2p"], o["prow"]; o["q2"] stays
-    zero)."""
+    zero); GMM1 also through megamoe_gmm1_gather_split, twice, into
+    o["gmC_split"] and o["gmC_split2"]."""
     assert gather or not paired
     d = MM.dims(w.M, w.K, w.E, w.top_k, w.I)
     R = w.R
@@ -69,6 +70,14 @@ def run_stages(w, dev: dict, w1p, w2p, debug_acc: bool = True, gather: bool = Fa
                                          ws)
         MM.megamoe_gmm1_gather(d, o["qx"], o["sorted_route"], o["expert_cumsum"], w1p,
                                dev["scale1"], o["gmC"], o.get("acc1"))
+        # GMM1 as the forward runs it (a sparse last round split over K), twice
+        # on one zero-filled buffer: the second call finds the counters the
+        # first one left
+        sws = torch.zeros(MM.megamoe_gmm1_split_workspace_bytes(d), dtype=torch.uint8, **cu)
+        for k in ("gmC_split", "gmC_split2"):
+            o[k] = torch.zeros((R, w.N1), dtype=torch.float16, **cu)
+            MM.megamoe_gmm1_gather_split(d, o["qx"], o["sorted_route"], o["expert_cumsum"], w1p,
+                                         dev["scale1"], o[k], sws)
         MM.megamoe_swiglu_quant_paired(d, o["gmC"], o["pts1"], o["expert_cumsum"], o["prow"],
                                        o["q2p"], o["pts2"])
         MM.megamoe_gmm2_paired(d, o["q2p"], o["expert_cumsum"], w2p, dev["scale2"],

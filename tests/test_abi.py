@@ -108,6 +108,10 @@ _POINTER_ARGS = {
     "megamoe_permute_noalloc": (9, ()),
     "megamoe_gmm1": (6, (5,)),
     "megamoe_gmm1_gather": (7, (6,)),
+    "megamoe_gmm1_gather_split": (7, ()),     # qx .. gmC, split buffer, then its size
+    "megamoe_permute_tokens_paired": (10, ()),
+    "megamoe_swiglu_quant_paired": (6, ()),
+    "megamoe_gmm2_paired": (6, (5,)),
     "megamoe_swiglu_quant": (5, ()),
     "megamoe_gmm2": (6, (5,)),
     "megamoe_unpermute": (5, ()),
@@ -133,7 +137,8 @@ def test_every_pointer_argument_checked(name):
     n_ptr, nullable = _POINTER_ARGS[name]
     d = MM.dims(16, 256, 4, 2, 128)
     good, odd = 0x10000, 0x10004
-    sized = name in ("megamoe_forward", "megamoe_permute", "megamoe_permute_tokens")
+    sized = name in ("megamoe_forward", "megamoe_permute", "megamoe_permute_tokens",
+                     "megamoe_permute_tokens_paired", "megamoe_gmm1_gather_split")
 
     def call(ptrs):
         args = [ctypes.byref(d)] + [ctypes.c_void_p(v) if v else None for v in ptrs]

@@ -142,7 +142,7 @@ def _compare_paired(w, g, gp):
     megamoe_*_paired) against the page's row-major q2: prow is each row plus
     the number of earlier experts with an odd row count, q2p holds every
     row's codes where prow puts them, and GMM2 and the combine give the same
-    bits."""
+    bits.  GMM1 with the K-split last round gives the page's gmC bits."""
     for k in ("sorted_route", "expanded_row_idx", "tokens_per_expert", "expert_cumsum"):
         assert torch.equal(gp[k], g[k]), k
     Rv = int(g["expert_cumsum"][-1].item()) if w.E else 0
@@ -160,6 +160,9 @@ def _compare_paired(w, g, gp):
     rows = q2p[(base[:, :, None] + np.arange(64)[None, None, :])].reshape(Rv, w.I)
     assert np.array_equal(rows, g["q2"][:Rv].cpu().numpy()), "q2p rows vs q2"
     assert torch.equal(gp["pts2"][:Rv], g["pts2"][:Rv]), "pts2"
+    # GMM1 with its sparse last round split over K (the forward's): the same bits
+    for k in ("gmC_split", "gmC_split2"):
+        assert torch.equal(gp[k][:Rv].view(torch.int16), g["gmC"][:Rv].view(torch.int16)), k
     assert torch.equal(gp["acc2"][:Rv], g["acc2"][:Rv]), "acc2"
     assert torch.equal(gp["gmm2_out"][:Rv].view(torch.int16), g["gmm2_out"][:Rv].view(torch.int16))
     assert torch.equal(gp["out"].view(torch.int16), g["out"].view(torch.int16)), "out"
@@ -211,6 +214,51 @@ def test_leftover_tiles_split_by_rows():
     out, dropped = H.run_forward(w, dev, w1p, w2p)
     assert dropped == 0
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
+
+
+def _last_round(tiles: int, grid: int) -> tuple[int, int, bool]:
+    """Full rounds F and leftover tiles L of the 256-row GEMM on `grid`
+    workgroups, and whether the leftovers are cut into pieces (at most one
+    tile per group of four workgroups)."""
+    F, L = tiles // grid, tiles % grid
+    return F, L, 1 <= L <= 8 * (grid // 8 // 4)
+
+
+@pytest.mark.parametrize("K", [512, 1536])
+def test_leftover_tiles_split_over_k(K):
+    """The forward's GMM1 with a sparse last round and K a multiple of 512:
+    each leftover tile runs as four K pieces on four workgroups of one XCD,
+    and the last piece to finish adds the four int32 partial tiles and stores
+    the tile.  60 experts with 300 rows (two m-blocks) and 196 with 130,
+    I = 128: 316 GMM1 tiles for 256 workgroups, so the 60 leftover tiles are
+    split, one K piece per workgroup; K = 512 gives each piece two K
+    slices (fewer than the copy ring's four stages), K = 1536 six.  Every
+    output element is compared with the oracle, the forward with the staged
+    run, and megamoe_gmm1_gather_split (twice on one buffer) with
+    megamoe_gmm1_gather."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hot, cold, E = 60, 196, 256
+    M = hot * 300 + cold * 130
+    w = W.custom(M, K, E, 1, 128, name=f"leftover_k{K}")
+    tiles = hot * 2 + cold
+    G = (min(cus, M // 256 + E) + 7) // 8 * 8      # the launch grid of the GEMM
+    F, L, split = _last_round(tiles, G)
+    assert F >= 1 and split and L <= 64, f"shape does not reach the K split on {cus} CUs"
+    print(f"[parity] {w.describe()} tiles {tiles} on {G} workgroups, {L} split", flush=True)
+    inp = W.generate(w, seed=6)
+    ids = np.concatenate([np.repeat(np.arange(hot), 300), hot + np.repeat(np.arange(cold), 130)])
+    inp["expert_idx"][:, 0] = np.random.default_rng(7).permutation(ids).astype(np.int32)
+    o_ref = O.forward(inp)
+    dev = H.to_dev(inp)
+    w1p, w2p = H.prepack(MM.dims(w.M, w.K, w.E, w.top_k, w.I), dev)
+    g = H.run_stages(w, dev, w1p, w2p)
+    torch.cuda.synchronize()
+    _compare_full(w, inp, o_ref, g)
+    _compare_paired(w, g, H.run_stages(w, dev, w1p, w2p, gather=True, paired=True))
+    for _ in range(2):  # the second forward reuses the counters the first one left
+        out, dropped = H.run_forward(w, dev, w1p, w2p)
+        assert dropped == 0
+        assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
 
 
 @pytest.mark.parametrize("hot,I,branch", [(20, 256, "pieces"), (25, 384, "plain_odd"),
