@@ -510,48 +510,57 @@ __device__ __forceinline__ int store_tile_private(const GmmParams &p, const v4i 
 }
 
 // A K piece of a leftover tile (sparse last round, GMM1 of the forward): the
-// tile's NP pieces each multiply a quarter of K and store their int32
-// partial tile to ks_part; the last piece to count itself adds the NP
-// partials (integer sums: exact, in any order) and stores the tile as
-// store_tile_private does.  No piece waits for another.  The protocol is
-// release / acquire at device scope around a system-scope counter: each
-// piece's partial is written back from its XCD's L2 before it counts itself,
-// and the last piece invalidates its caches before it reads the partials.
-// It also puts the counter back to zero, so a buffer zeroed once serves every
-// later launch.  The last piece reads its own partial back too, so that its accumulators
-// are free during the sums (the K loop leaves no register for another copy
-// of them).  Returns the store instructions issued.
+// tile's NP pieces each multiply 1 / NP of K and store their int32 partial
+// tile to ks_part; the last piece to count itself adds the NP partials
+// (integer sums: exact, in any order) and stores the tile as
+// store_tile_private does.  No piece waits for another.
+//
+// The partials cross CUs (and, were the pieces dealt to different XCDs, L2
+// caches) as device-scope atomic stores and loads, which the hardware makes
+// coherent line by line (the sc1 policy) instead of by writing back or
+// invalidating a whole L2: the fences that would do that also dropped the
+// cached operands of every other workgroup on the XCD.  Each wave's partial
+// stores have completed (vmcnt 0) before the workgroup barrier that precedes
+// its counter increment, and the last piece issues its loads only after its
+// increment has returned the count of the other pieces.  The last piece also
+// puts the counter back to zero, so a buffer zeroed once serves every later
+// launch.  It reads its own partial back too, so that its accumulators are
+// free during the sums (the K loop leaves no register for the other pieces'
+// blocks beside them).  Returns the store instructions issued.
 template <int TM, int TN, int NW, int NP>
 __device__ __forceinline__ int ks_store_tile(const GmmParams &p, const v4i (&acc)[TM][TN], int jj,
                                              int piece, int wave, const float *s_sc, int row0,
                                              int n0, int wm0, int wn0, int8_t *wbuf, int r_lo,
                                              int r_hi, bool live, int *s_flag) {
-    constexpr int kPiece = NW * TM * TN * kWave;  // 16-byte units of one partial tile
-    static_assert(kPiece * 16 <= (int)kKsPartBytes, "partial tile size");
+    constexpr int kPiece = NW * TM * TN * 4 * kWave;  // 32-bit words of one partial tile
+    static_assert(kPiece * 4 <= (int)kKsPartBytes, "partial tile size");
     live = live && n0 + wn0 < p.N;
     const int lane = fresh_lane_id();
-    // [piece][wave][16x16 block][lane]: each store writes 1 KB
-    const v4i *part = reinterpret_cast<const v4i *>(p.ks_part) + (size_t)jj * NP * kPiece +
-                      (size_t)wave * TM * TN * kWave + lane;
+    // [piece][wave][16x16 block][accumulator c][lane]: 256 contiguous bytes
+    // per instruction
+    uint32_t *part = reinterpret_cast<uint32_t *>(p.ks_part) + (size_t)jj * NP * kPiece +
+                     (size_t)wave * TM * TN * 4 * kWave + lane;
     // a wave without an output row neither writes nor reads
     if (live) {
-        v4i *mine = const_cast<v4i *>(part) + (size_t)piece * kPiece;
+        uint32_t *mine = part + (size_t)piece * kPiece;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) mine[(i * TN + j) * kWave] = acc[i][j];
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    __hip_atomic_store(mine + ((i * TN + j) * 4 + c) * kWave,
+                                       (uint32_t)acc[i][j][c], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is in L2
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is stored
     __syncthreads();
     if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         *s_flag = (int)__hip_atomic_fetch_add(p.ks_count + jj, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_SYSTEM);
-        if (*s_flag == NP - 1) {
-            // every piece has counted: the counter is free for the next launch
-            __hip_atomic_store(p.ks_count + jj, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        }
+                                              __HIP_MEMORY_SCOPE_AGENT);
+        // every piece has counted: the counter is free for the next launch
+        if (*s_flag == NP - 1)
+            __hip_atomic_store(p.ks_count + jj, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (*s_flag != NP - 1 || !live) return 0;  // another piece of the tile stores it
@@ -566,7 +575,12 @@ __device__ __forceinline__ int ks_store_tile(const GmmParams &p, const v4i (&acc
 #pragma unroll
         for (int q = 0; q < NP; ++q)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) t[q][j] = part[(size_t)q * kPiece + (i * TN + j) * kWave];
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    t[q][j][c] = (int)__hip_atomic_load(
+                        part + (size_t)q * kPiece + ((i * TN + j) * 4 + c) * kWave,
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int q = 1; q < NP; ++q)
 #pragma unroll
@@ -706,8 +720,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N *kWave) void gmm_i8_ring_kernel(Gm
     // With a partial-tile buffer (the forward's GMM1), the pieces of a
     // leftover tile split its K slices instead of its rows: each runs a
     // quarter of the K chain that bounds a row piece, and the last of them
-    // adds the partial tiles (ks_combine).
-    const bool ksplit = ranked && p.ks_part != nullptr && p.acc_dbg == nullptr &&
+    // adds the partial tiles (ks_store_tile).
+    const bool ksplit = !TRIM && ranked && p.ks_part != nullptr && p.acc_dbg == nullptr &&
                         nst % (2 * WAVES_M) == 0 && L <= kKsMaxTiles;
 
     // SwiGLU in the last round (GMM1 of the forward; tiles of unequal cost).

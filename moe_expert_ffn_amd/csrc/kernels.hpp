@@ -6,13 +6,15 @@
 
 namespace megamoe {
 
-// K-split last round of the 256-row GEMM: at most this many leftover tiles,
-// each in 4 pieces whose int32 partial tiles are 256 KB
+// K-split last round of the 256-row GEMM: at most kKsMaxTiles leftover tiles
+// in 4 pieces, whose int32 partial tiles take at most 256 KB each; one
+// counter per tile
 constexpr int kKsMaxTiles = 64;
+constexpr int kKsCounters = kKsMaxTiles;
 constexpr size_t kKsPartBytes = 256 * 256 * 4;
 // words of the forward's sync array: 3 for SwiGLU in GMM1's last round, then
-// one counter per K-split leftover tile; the permute zeroes them
-constexpr int kSyncWords = 3 + kKsMaxTiles;
+// the K-split counters; the permute zeroes them
+constexpr int kSyncWords = 3 + kKsCounters;
 
 struct GmmParams {
     const int8_t *A;          // [rows, Kred] expert-major activations
@@ -37,10 +39,11 @@ struct GmmParams {
     int tail_I = 0;
     int tail_spin = 0;                // poll limit of the wait; < 0: give up at once
     const int32_t *tail_prow = nullptr;  // nullable: q2 row-paired (see a_pair), row r at tail_prow[r]
-    // GMM1 of the forward, nullable: a sparse last round's leftover tiles are
-    // split over K instead of into row pieces (see gmm.hip).  ks_part holds
-    // kKsMaxTiles x 4 int32 partial tiles (kKsPartBytes each); ks_count
-    // kKsMaxTiles counters, zero at launch (the kernel leaves them at zero).
+    // GMM1 of the forward, nullable: a sparse last round's leftover
+    // tiles are split over K instead of into row pieces (see gmm.hip).
+    // ks_part holds kKsMaxTiles x 4 int32 partial tiles (kKsPartBytes each);
+    // ks_count kKsCounters counters, zero at launch (the kernel leaves them
+    // at zero).
     int32_t *ks_part = nullptr;
     uint32_t *ks_count = nullptr;
     // A in the row-paired layout (GEMMs without a_route): every expert's group

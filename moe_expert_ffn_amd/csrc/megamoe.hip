@@ -86,8 +86,7 @@ size_t permute_ws_bytes(const megamoe_dims &d) {
 
 // GMM1's K-split buffer (megamoe_gmm1_gather_split): the tile counters, then
 // the partial tiles
-constexpr size_t kSplitCountBytes = 256;
-static_assert(kKsMaxTiles * 4 <= (int)kSplitCountBytes, "counter block");
+constexpr size_t kSplitCountBytes = (kKsCounters * 4 + 255) / 256 * 256;
 size_t split_ws_bytes() { return kSplitCountBytes + (size_t)kKsMaxTiles * 4 * kKsPartBytes; }
 
 // bytes of q2 in the row-paired layout: each expert's rows padded to an even

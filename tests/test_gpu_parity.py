@@ -216,35 +216,50 @@ def test_leftover_tiles_split_by_rows():
     assert np.array_equal(H.bf16_bits(out), H.bf16_bits(g["out"]))
 
 
-def _last_round(tiles: int, grid: int) -> tuple[int, int, bool]:
-    """Full rounds F and leftover tiles L of the 256-row GEMM on `grid`
-    workgroups, and whether the leftovers are cut into pieces (at most one
-    tile per group of four workgroups)."""
-    F, L = tiles // grid, tiles % grid
-    return F, L, 1 <= L <= 8 * (grid // 8 // 4)
+def _last_round_mode(rows_per_expert, N, Kred, cus):
+    """How the 256-row GEMM (one workgroup per CU) deals its last round when
+    the forward passes it a partial-tile buffer: "none" (a full round or no
+    leftover), "k4" (leftover tiles in four K pieces), "rows" (four row
+    pieces: K slices not a multiple of 8) or "whole" (one workgroup per
+    leftover tile)."""
+    NB = (N + 255) // 256
+    E = len(rows_per_expert)
+    R = int(sum(rows_per_expert))
+    tiles = sum((r + 255) // 256 for r in rows_per_expert) * NB
+    G = (min(cus, (R // 256 + E) * NB) + 7) // 8 * 8
+    F, L = tiles // G, tiles % G
+    nst, act = Kred // 64, G // 8
+    if L == 0:
+        return "none", F, L
+    if L <= 8 * (act // 4):
+        return ("k4" if nst % 8 == 0 and L <= 64 else "rows"), F, L
+    return "whole", F, L
 
 
-@pytest.mark.parametrize("K", [512, 1536])
-def test_leftover_tiles_split_over_k(K):
-    """The forward's GMM1 with a sparse last round and K a multiple of 512:
-    each leftover tile runs as four K pieces on four workgroups of one XCD,
-    and the last piece to finish adds the four int32 partial tiles and stores
-    the tile.  60 experts with 300 rows (two m-blocks) and 196 with 130,
-    I = 128: 316 GMM1 tiles for 256 workgroups, so the 60 leftover tiles are
-    split, one K piece per workgroup; K = 512 gives each piece two K
-    slices (fewer than the copy ring's four stages), K = 1536 six.  Every
-    output element is compared with the oracle, the forward with the staged
-    run, and megamoe_gmm1_gather_split (twice on one buffer) with
-    megamoe_gmm1_gather."""
+@pytest.mark.parametrize("hot,K,I,mode", [
+    (60, 256, 128, "rows"), (60, 512, 128, "k4"), (60, 1536, 128, "k4"),
+    (20, 1024, 128, "k4"), (100, 512, 128, "whole")])
+def test_leftover_tiles_split_over_k(hot, K, I, mode):
+    """The forward's GMM1 with a sparse last round: each leftover tile runs on
+    four workgroups of one XCD as four quarters of its K slices (a round up to
+    a quarter full); the last piece to finish adds the int32 partial tiles
+    and stores the tile.  `hot` experts with 300 rows (two m-blocks) and the
+    rest of 256 with 130; GMM1 is asserted to take `mode`.  At K = 256 GMM1
+    has 4 K slices, too few for quarters, and cuts row pieces instead; at 512
+    each quarter has two K slices (fewer than the copy ring's four stages),
+    at 1024 four, at 1536 six; 100 leftover tiles are more than a quarter
+    round and stay whole.  Every output element is compared with the oracle,
+    the forward with the staged run, and megamoe_gmm1_gather_split (twice on
+    one buffer) with megamoe_gmm1_gather."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    hot, cold, E = 60, 196, 256
-    M = hot * 300 + cold * 130
-    w = W.custom(M, K, E, 1, 128, name=f"leftover_k{K}")
-    tiles = hot * 2 + cold
-    G = (min(cus, M // 256 + E) + 7) // 8 * 8      # the launch grid of the GEMM
-    F, L, split = _last_round(tiles, G)
-    assert F >= 1 and split and L <= 64, f"shape does not reach the K split on {cus} CUs"
-    print(f"[parity] {w.describe()} tiles {tiles} on {G} workgroups, {L} split", flush=True)
+    E = 256
+    cold = E - hot
+    rows = [300] * hot + [130] * cold
+    M = sum(rows)
+    w = W.custom(M, K, E, 1, I, name=f"leftover_{hot}_{K}_{I}")
+    got, F, L = _last_round_mode(rows, 2 * I, K, cus)
+    assert got == mode and F >= 1, f"GMM1 takes {got} (F={F}, L={L}) on {cus} CUs"
+    print(f"[parity] {w.describe()} GMM1: {F} rounds + {L} tiles as {mode}", flush=True)
     inp = W.generate(w, seed=6)
     ids = np.concatenate([np.repeat(np.arange(hot), 300), hot + np.repeat(np.arange(cold), 130)])
     inp["expert_idx"][:, 0] = np.random.default_rng(7).permutation(ids).astype(np.int32)
