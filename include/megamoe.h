@@ -174,7 +174,7 @@ int megamoe_gmm1_gather(const megamoe_dims *d, const int8_t *qx, const int32_t *
  * by four workgroups over a quarter of K each, and the last of them adds the
  * four int32 partial tiles (an exact integer sum, section 3's acc) and stores
  * the tile.  Results equal megamoe_gmm1_gather's bit for bit.
- *   megamoe_gmm1_split_workspace_bytes: size of split_ws (about 64 MB).
+ *   megamoe_gmm1_split_workspace_bytes: size of split_ws (about 67 MB).
  *   split_ws  device, zero-filled before its first use; each call leaves it
  *             ready for the next (its counters back at zero).  Calls that
  *             overlap in time on one split_ws race; give concurrent streams
