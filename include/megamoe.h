@@ -65,7 +65,8 @@ int megamoe_check_dims(const megamoe_dims *d);
  * stage overview passes from stage to stage (the FrontReorder metadata and
  * per-token scales of section 1, GMM1's fp16 output of section 3, SwiGLU's
  * int8 rows and scales of section 4, GMM2's output of section 5) plus the
- * device error word.  megamoe_permute needs only
+ * device error word and GMM1's partial tiles for a last round split over K
+ * (megamoe_gmm1_gather_split).  megamoe_permute needs only
  * megamoe_permute_workspace_bytes (error word, sort scratch). */
 int megamoe_workspace_bytes(const megamoe_dims *d, size_t *bytes);
 int megamoe_permute_workspace_bytes(const megamoe_dims *d, size_t *bytes);
