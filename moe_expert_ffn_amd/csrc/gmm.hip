@@ -431,20 +431,10 @@ __device__ __forceinline__ int fresh_lane_id() {
     return l;
 }
 
-// The tile's output, dequantised to fp16 (fp32(acc) * scale, rounded to
-// fp32, then to fp16), stored in whole 128-byte lines without the ring and
-// without a workgroup barrier.  Each wave passes its 64 x 64 sub-tile through
-// its own 1 KB of LDS, 8 rows at a time: the 32 lanes that hold a chunk's 8
-// rows in the MFMA layout write them there (16-byte piece c of row rr at
-// slot c ^ rr, free of bank conflicts for both the 8-byte writes and the
-// row reads), then every lane reads one 16-byte piece of one row and the
-// wave stores 8 whole rows with one instruction.  A wave's LDS operations
-// complete in order, so no wait is needed between a chunk's writes and reads.
-// Since the ring is not used, the next tile's first copies can be in flight
-// while these stores go out.  Returns the number of store instructions
-// issued (wave-uniform).
-// rows 16 i .. 16 i + 15 of a wave's sub-tile from the lane's accumulators
-// a[TN] of them (MFMA layout); returns the store instructions issued
+// One row group of a wave's sub-tile (rows 16 i .. 16 i + 15), dequantised
+// and stored as described at store_tile_private below, from the lane's
+// accumulators a[TN] of those rows (MFMA layout).  Returns the store
+// instructions issued.
 template <int TN>
 __device__ __forceinline__ int store_group(const GmmParams &p, const v4i (&a)[TN], int i,
                                            const float *s_sc, int row0, int n0, int wm0, int wn0,
@@ -491,6 +481,18 @@ __device__ __forceinline__ bool group_live(int i, int wm0, int r_lo, int r_hi) {
     return rb0 + 16 > r_lo && rb0 < r_hi;
 }
 
+// The tile's output, dequantised to fp16 (fp32(acc) * scale, rounded to
+// fp32, then to fp16), stored in whole 128-byte lines without the ring and
+// without a workgroup barrier.  Each wave passes its 64 x 64 sub-tile through
+// its own 1 KB of LDS, 8 rows at a time: the 32 lanes that hold a chunk's 8
+// rows in the MFMA layout write them there (16-byte piece c of row rr at
+// slot c ^ rr, free of bank conflicts for both the 8-byte writes and the
+// row reads), then every lane reads one 16-byte piece of one row and the
+// wave stores 8 whole rows with one instruction.  A wave's LDS operations
+// complete in order, so no wait is needed between a chunk's writes and reads.
+// Since the ring is not used, the next tile's first copies can be in flight
+// while these stores go out.  Returns the number of store instructions
+// issued (wave-uniform).
 template <int TM, int TN>
 __device__ __forceinline__ int store_tile_private(const GmmParams &p, const v4i (&acc)[TM][TN],
                                                   const float *s_sc, int row0, int n0, int wm0,
