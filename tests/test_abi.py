@@ -80,6 +80,24 @@ def test_null_and_misaligned_pointers_rejected():
     # workspace too small is reported before anything is launched
     rc = lib.megamoe_forward(ctypes.byref(d), *([good] * 9), ctypes.c_size_t(16), None)
     assert rc == 3
+    # the same for GMM1's K-split buffer: one byte short of its size
+    need = MM.megamoe_gmm1_split_workspace_bytes(d)
+    rc = lib.megamoe_gmm1_gather_split(ctypes.byref(d), *([good] * 7), ctypes.c_size_t(need - 1),
+                                       None)
+    assert rc == 3
+
+
+def test_split_workspace_size():
+    """GMM1's K-split buffer holds a counter block and 4 partial int32 tiles of
+    256 x 256 for each of up to 64 leftover tiles, whatever the dims."""
+    sizes = {MM.megamoe_gmm1_split_workspace_bytes(MM.dims(*a))
+             for a in ((16, 256, 4, 2, 128), (2048, 7168, 32, 8, 2048), (4096, 4096, 64, 6, 1408))}
+    assert len(sizes) == 1
+    (n,) = sizes
+    assert 64 * 4 * 256 * 256 * 4 < n <= 64 * 4 * 256 * 256 * 4 + 4096
+    # the forward's workspace holds the same partial tiles
+    d = MM.dims(2048, 7168, 32, 8, 2048)
+    assert MM.megamoe_workspace_bytes(d) > 64 * 4 * 256 * 256 * 4 + 2048 * 8 * 7168 * 2
 
 
 def test_set_overlap_modes():
