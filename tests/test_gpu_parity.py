@@ -236,15 +236,18 @@ def _last_round_mode(rows_per_expert, N, Kred, cus):
     return "whole", F, L
 
 
-@pytest.mark.parametrize("hot,K,I,mode", [
-    (60, 256, 128, "rows"), (60, 512, 128, "k4"), (60, 1536, 128, "k4"),
-    (20, 1024, 128, "k4"), (100, 512, 128, "whole")])
-def test_leftover_tiles_split_over_k(hot, K, I, mode):
+@pytest.mark.parametrize("hot,K,I,mode,hot_rows", [
+    (60, 256, 128, "rows", 300), (60, 512, 128, "k4", 300), (60, 1536, 128, "k4", 300),
+    (20, 1024, 128, "k4", 300), (100, 512, 128, "whole", 300), (60, 512, 128, "k4", 257)])
+def test_leftover_tiles_split_over_k(hot, K, I, mode, hot_rows):
     """The forward's GMM1 with a sparse last round: each leftover tile runs on
     four workgroups of one XCD as four quarters of its K slices (a round up to
     a quarter full); the last piece to finish adds the int32 partial tiles
-    and stores the tile.  `hot` experts with 300 rows (two m-blocks) and the
-    rest of 256 with 130; GMM1 is asserted to take `mode`.  At K = 256 GMM1
+    and stores the tile.  `hot` experts with `hot_rows` rows (two m-blocks:
+    192 rows and the rest, which are the leftover tiles) and the rest of 256
+    with 130; GMM1 is asserted to take `mode`.  With 257 rows a leftover tile
+    has 65 rows, so one wave row block of each piece holds a single live row.
+    At K = 256 GMM1
     has 4 K slices, too few for quarters, and cuts row pieces instead; at 512
     each quarter has two K slices (fewer than the copy ring's four stages),
     at 1024 four, at 1536 six; 100 leftover tiles are more than a quarter
@@ -254,14 +257,15 @@ def test_leftover_tiles_split_over_k(hot, K, I, mode):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     E = 256
     cold = E - hot
-    rows = [300] * hot + [130] * cold
+    rows = [hot_rows] * hot + [130] * cold
     M = sum(rows)
-    w = W.custom(M, K, E, 1, I, name=f"leftover_{hot}_{K}_{I}")
+    w = W.custom(M, K, E, 1, I, name=f"leftover_{hot}x{hot_rows}_{K}_{I}")
     got, F, L = _last_round_mode(rows, 2 * I, K, cus)
     assert got == mode and F >= 1, f"GMM1 takes {got} (F={F}, L={L}) on {cus} CUs"
     print(f"[parity] {w.describe()} GMM1: {F} rounds + {L} tiles as {mode}", flush=True)
     inp = W.generate(w, seed=6)
-    ids = np.concatenate([np.repeat(np.arange(hot), 300), hot + np.repeat(np.arange(cold), 130)])
+    ids = np.concatenate([np.repeat(np.arange(hot), hot_rows),
+                          hot + np.repeat(np.arange(cold), 130)])
     inp["expert_idx"][:, 0] = np.random.default_rng(7).permutation(ids).astype(np.int32)
     o_ref = O.forward(inp)
     dev = H.to_dev(inp)
